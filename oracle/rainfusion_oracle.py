@@ -1,0 +1,267 @@
+"""Plain fp64 CPU oracle for RainFusion2.0's online block-sparse attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+benchmark's CPU-baseline leg may import this module.  It shares no code with
+the HIP library or its Python binding, and imports nothing from them.
+
+Sources (cited by page title and section; no line numbers):
+  [RF2]  "RainFusion2.0: Temporal-Spatial Awareness and Hardware-Efficient
+         Block-wise Sparse Attention" (arXiv 2512.24086): Abstract, key
+         insights (1) block-wise mean values as representative tokens for
+         sparse mask prediction, (2) spatiotemporal-aware token permutation,
+         (3) first-frame sink; TL;DR ("3D window permutation"); Figure 3
+         caption (80% sparsity with and without the 3D permutation).
+  [RF1]  "RainFusion: Adaptive Video Generation Acceleration via
+         Multi-Dimensional Visual Redundancy" (arXiv 2505.21036): Abstract;
+         the pith.science review's "Assumptions" list (softmax attention,
+         Eq. (1)) and "What carries the argument" (masked recall R').
+
+The pages give no formula for the mask rule, the permutation order or the
+kernel.  Where they are silent this module takes the readings listed here;
+each function restates the one it uses.
+  R1  Window order: blocks in row-major order of (bt, bh, bw), tokens inside
+      a block in row-major order of (dt, dh, dw); the grid is padded up to a
+      multiple of the window along each axis; pad slots hold zeros.
+  R2  Raster mode (permutation off): slot = raster token index; blocks are
+      runs of bs consecutive tokens; the last block is padded.
+  R3  Representative token of a block = arithmetic mean over its valid
+      (non-pad) tokens, per batch and head.
+  R4  Block score l_ij = Qbar_i . Kbar_j / sqrt(d); P = row softmax of l over
+      video key blocks.  Ranking by l equals ranking by P.
+  R5  Keep rule per video query-block row: n = video key blocks,
+      k = floor((n (100 - s) + 50) / 100), S = first-frame sink blocks,
+      k_eff = max(k, |S|, 1); kept = S plus the k_eff - |S| highest-scoring
+      non-sink blocks, ties to the lower block index.
+  R6  First frame = latent frame 0; sink = every key block holding a frame-0
+      token (only when the sink is switched on).
+  R7  Text tokens follow the video tokens, form ceil(n_text / bs) tiles, are
+      not pooled, are appended to every video row's kept list, and text
+      query tiles attend to every tile.
+  R8  Attention: o = sum_j softmax_j(q . k_j / sqrt(d)) v_j over the valid
+      tokens of the row's kept tiles; pad query rows are 0.
+"""
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Layout:
+    """Latent grid (T frames of H x W tokens), window, text and switches."""
+    T: int
+    H: int
+    W: int
+    wt: int
+    wh: int
+    ww: int
+    n_text: int = 0
+    permute: int = 1
+    sink: int = 0
+
+
+def _ceil_div(a, b):
+    return -(-a // b)
+
+
+def sizes(lay: Layout) -> dict:
+    """Derived sizes of a layout.  [RF2 TL;DR, 3D window permutation] with
+    readings R1 (padding to whole windows), R2 (raster blocks) and R7."""
+    bs = lay.wt * lay.wh * lay.ww
+    N = lay.T * lay.H * lay.W
+    if lay.permute:
+        nT, nH, nW = (_ceil_div(lay.T, lay.wt), _ceil_div(lay.H, lay.wh),
+                      _ceil_div(lay.W, lay.ww))
+        Np = nT * nH * nW * bs
+        nb = nT * nH * nW
+    else:
+        nT = nH = nW = 0
+        nb = _ceil_div(N, bs)
+        Np = nb * bs
+    n_tt = _ceil_div(lay.n_text, bs)
+    return dict(bs=bs, N=N, Np=Np, nb=nb, nT=nT, nH=nH, nW=nW,
+                n_text=lay.n_text, n_text_tiles=n_tt, n_tiles=nb + n_tt,
+                L=N + lay.n_text, Lp=Np + lay.n_text)
+
+
+def slot_of_token(lay: Layout) -> np.ndarray:
+    """pi(n): the slot of raster token n = (t H + h) W + w.
+
+    [RF2 Abstract, insight (2); TL;DR "3D window permutation"], reading R1:
+    t = bt wt + dt (same for h, w), block = (bt nH + bh) nW + bw,
+    slot = block bs + (dt wh + dh) ww + dw.  Reading R2 when the permutation
+    is off: slot = n."""
+    z = sizes(lay)
+    if not lay.permute:
+        return np.arange(z["N"], dtype=np.int64)
+    t, h, w = np.meshgrid(np.arange(lay.T), np.arange(lay.H), np.arange(lay.W),
+                          indexing="ij")
+    bt, dt = np.divmod(t, lay.wt)
+    bh, dh = np.divmod(h, lay.wh)
+    bw, dw = np.divmod(w, lay.ww)
+    block = (bt * z["nH"] + bh) * z["nW"] + bw
+    inner = (dt * lay.wh + dh) * lay.ww + dw
+    return (block * z["bs"] + inner).reshape(-1).astype(np.int64)
+
+
+def slot_valid(lay: Layout) -> np.ndarray:
+    """Boolean per slot of the permuted sequence (video slots, then text):
+    True where the slot holds a real token.  Readings R1, R2, R7."""
+    z = sizes(lay)
+    valid = np.zeros(z["Lp"], dtype=bool)
+    valid[slot_of_token(lay)] = True
+    valid[z["Np"]:] = True
+    return valid
+
+
+def permute(x: np.ndarray, lay: Layout) -> np.ndarray:
+    """Scatter raster tokens into window order.  x: [..., N + n_text, d] ->
+    [..., Np + n_text, d]; pad slots 0; text copied after Np.
+    [RF2 Abstract, insight (2)], readings R1, R2, R7."""
+    z = sizes(lay)
+    out = np.zeros(x.shape[:-2] + (z["Lp"], x.shape[-1]), dtype=x.dtype)
+    out[..., slot_of_token(lay), :] = x[..., :z["N"], :]
+    out[..., z["Np"]:, :] = x[..., z["N"]:, :]
+    return out
+
+
+def unpermute(xp: np.ndarray, lay: Layout) -> np.ndarray:
+    """Inverse of `permute`: gather each raster token from its slot; pad
+    dropped, text copied back.  [RF2 Abstract, insight (2)]."""
+    z = sizes(lay)
+    out = np.empty(xp.shape[:-2] + (z["L"], xp.shape[-1]), dtype=xp.dtype)
+    out[..., :z["N"], :] = xp[..., slot_of_token(lay), :]
+    out[..., z["N"]:, :] = xp[..., z["Np"]:, :]
+    return out
+
+
+def block_counts(lay: Layout) -> np.ndarray:
+    """c_b: valid tokens in each video block."""
+    z = sizes(lay)
+    return slot_valid(lay)[:z["Np"]].reshape(z["nb"], z["bs"]).sum(axis=1)
+
+
+def block_means(xp: np.ndarray, lay: Layout) -> np.ndarray:
+    """Representative token of each video block: the mean of its valid
+    tokens, in fp64.  [RF2 Abstract, insight (1)], reading R3.
+    xp: [B, H, Np + n_text, d] -> [B, H, nb, d]."""
+    z = sizes(lay)
+    valid = slot_valid(lay)[:z["Np"]].reshape(z["nb"], z["bs"])
+    blocks = xp[..., :z["Np"], :].astype(np.float64)
+    blocks = blocks.reshape(xp.shape[:-2] + (z["nb"], z["bs"], xp.shape[-1]))
+    sums = (blocks * valid[:, :, None]).sum(axis=-2)
+    return sums / valid.sum(axis=1)[:, None]
+
+
+def block_scores(qbar: np.ndarray, kbar: np.ndarray):
+    """Block logits l = Qbar Kbar^T / sqrt(d) and their row softmax P over
+    the video key blocks, fp64.  [RF2 Abstract, insight (1)], reading R4."""
+    d = qbar.shape[-1]
+    l = np.matmul(qbar, np.swapaxes(kbar, -1, -2)) / math.sqrt(d)
+    e = np.exp(l - l.max(axis=-1, keepdims=True))
+    return l, e / e.sum(axis=-1, keepdims=True)
+
+
+def sink_blocks(lay: Layout) -> np.ndarray:
+    """Ascending ids of the key blocks that hold a frame-0 token, or none when
+    the sink is off.  [RF2 Abstract, insight (3) first-frame sink], R6."""
+    if not lay.sink:
+        return np.zeros(0, dtype=np.int64)
+    z = sizes(lay)
+    first = slot_of_token(lay)[: lay.H * lay.W]
+    return np.unique(first // z["bs"])
+
+
+def keep_count(n: int, sparsity_pct: int, n_sink: int):
+    """(k, k_eff) of reading R5, in integer arithmetic."""
+    k = (n * (100 - sparsity_pct) + 50) // 100
+    return k, max(k, n_sink, 1)
+
+
+def predict_mask(qbar: np.ndarray, kbar: np.ndarray, lay: Layout,
+                 sparsity_pct: int):
+    """Kept key tiles per query tile, for every (b, h).
+
+    Returns (kept, l): kept[b][h] is a list over query tiles (video blocks,
+    then text tiles) of ascending int arrays of key-tile ids (video blocks
+    0..nb-1, text tiles nb..); l is the logit array [B, H, nb, nb].
+    [RF2 Abstract, insights (1) and (3); TL;DR], readings R4-R7."""
+    z = sizes(lay)
+    nb, n_tt = z["nb"], z["n_text_tiles"]
+    l, _ = block_scores(qbar, kbar)
+    sinks = sink_blocks(lay)
+    is_sink = np.zeros(nb, dtype=bool)
+    is_sink[sinks] = True
+    _, k_eff = keep_count(nb, sparsity_pct, len(sinks))
+    n_pick = k_eff - len(sinks)
+    text_tiles = np.arange(nb, nb + n_tt)
+    all_tiles = np.arange(nb + n_tt)
+    idx = np.arange(nb)
+    kept = []
+    B, H = qbar.shape[:2]
+    for b in range(B):
+        per_head = []
+        for h in range(H):
+            rows = []
+            for i in range(nb):
+                cand = idx[~is_sink]
+                order = np.lexsort((cand, -l[b, h, i, cand]))
+                chosen = np.concatenate([sinks, cand[order[:n_pick]]])
+                rows.append(np.concatenate([np.sort(chosen), text_tiles]))
+            for _ in range(n_tt):
+                rows.append(all_tiles.copy())
+            per_head.append(rows)
+        kept.append(per_head)
+    return kept, l
+
+
+def sparse_attention(qp, kp, vp, kept, lay: Layout, scale=None,
+                     query_tiles=None):
+    """Block-sparse softmax attention over the kept tiles, fp64.
+
+    For each valid query token of tile i: o = sum_j softmax_j(q . k_j * scale)
+    v_j over the valid tokens of the tiles in kept[b][h][i]; pad query rows
+    are 0.  [RF2 Abstract, skipping insignificant tokens; RF1 review,
+    Assumptions, Eq. (1) softmax attention], reading R8.
+
+    qp, kp, vp: [B, H, Np + n_text, d] in window order.  query_tiles: None
+    (all) or a dict {(b, h): iterable of tile ids}.  Tiles not computed are
+    NaN in the result so that an accidental comparison fails."""
+    z = sizes(lay)
+    bs, Lp = z["bs"], z["Lp"]
+    d = qp.shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    valid = slot_valid(lay)
+    B, H = qp.shape[:2]
+    out = np.full(qp.shape, np.nan, dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            tiles = (range(z["n_tiles"]) if query_tiles is None
+                     else query_tiles.get((b, h), ()))
+            for i in tiles:
+                rows = np.arange(i * bs, min((i + 1) * bs, Lp))
+                out[b, h, rows] = 0.0
+                qrows = rows[valid[rows]]
+                keys = np.concatenate([
+                    np.arange(j * bs, min((j + 1) * bs, Lp))
+                    for j in kept[b][h][i]])
+                keys = keys[valid[keys]]
+                q = qp[b, h, qrows].astype(np.float64)
+                k = kp[b, h, keys].astype(np.float64)
+                v = vp[b, h, keys].astype(np.float64)
+                s = (q @ k.T) * scale
+                p = np.exp(s - s.max(axis=1, keepdims=True))
+                out[b, h, qrows] = (p @ v) / p.sum(axis=1, keepdims=True)
+    return out
+
+
+def run(q, k, v, lay: Layout, sparsity_pct: int, query_tiles=None):
+    """The whole path on raster inputs [B, H, N + n_text, d] (any float
+    dtype; computed in fp64): permute, pool, predict, attend, unpermute."""
+    qp, kp, vp = (permute(np.asarray(x, dtype=np.float64), lay)
+                  for x in (q, k, v))
+    qbar, kbar = block_means(qp, lay), block_means(kp, lay)
+    kept, l = predict_mask(qbar, kbar, lay, sparsity_pct)
+    op = sparse_attention(qp, kp, vp, kept, lay, query_tiles=query_tiles)
+    return dict(qp=qp, kp=kp, vp=vp, qbar=qbar, kbar=kbar, l=l, kept=kept,
+                op=op, o=unpermute(op, lay))

@@ -1,0 +1,409 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: hand-worked
+fixtures, a constructive enumeration of the window order, closed forms,
+invariants, special cases that reduce to textbook dense attention, and brute
+force on tiny inputs.  No GPU is needed.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+from hypothesis import given, settings, strategies as st
+
+from oracle import rainfusion_oracle as orc
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_golden(name):
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, *vals = line.split()
+            out[key] = [int(v) for v in vals]
+    return out
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+# ---------------------------------------------------------------- permutation
+
+@pytest.mark.parametrize("name", ["slots_T2H3W4_win1x2x2.txt",
+                                  "slots_T3H2W3_win2x1x3.txt"])
+def test_slots_match_hand_worked_fixture(name):
+    g = _read_golden(name)
+    lay = orc.Layout(g["T"][0], g["H"][0], g["W"][0], g["wt"][0], g["wh"][0],
+                     g["ww"][0], sink=1)
+    z = orc.sizes(lay)
+    assert z["Np"] == g["Np"][0] and z["nb"] == g["nb"][0]
+    assert orc.slot_of_token(lay).tolist() == g["slots"]
+    assert orc.block_counts(lay).tolist() == g["counts"]
+    assert orc.sink_blocks(lay).tolist() == g["sinks"]
+
+
+def test_tiny_workload_slots_by_hand():
+    # 3x16x16 grid, 1x8x8 windows: 2x2 blocks per frame of 64 tokens.
+    lay = orc.Layout(3, 16, 16, 1, 8, 8, sink=1)
+    slot = orc.slot_of_token(lay)
+    n = lambda t, h, w: (t * 16 + h) * 16 + w
+    assert slot[n(0, 0, 8)] == 64
+    assert slot[n(0, 8, 0)] == 128
+    assert slot[n(1, 0, 0)] == 256
+    assert slot[n(0, 1, 0)] == 8
+    assert slot[n(2, 15, 15)] == 767
+    assert orc.sink_blocks(lay).tolist() == [0, 1, 2, 3]
+
+
+def _enumerate_window_order(lay):
+    """Slot sequence built constructively: walk the padded grid window by
+    window (frames outermost), and inside each window row-major; record which
+    raster token (or pad) lands in each successive slot."""
+    T, H, W, wt, wh, ww = lay.T, lay.H, lay.W, lay.wt, lay.wh, lay.ww
+    src = []
+    for t0 in range(0, math.ceil(T / wt) * wt, wt):
+        for h0 in range(0, math.ceil(H / wh) * wh, wh):
+            for w0 in range(0, math.ceil(W / ww) * ww, ww):
+                for t in range(t0, t0 + wt):
+                    for h in range(h0, h0 + wh):
+                        for w in range(w0, w0 + ww):
+                            ok = t < T and h < H and w < W
+                            src.append((t * H + h) * W + w if ok else -1)
+    return src
+
+
+@pytest.mark.parametrize("dims", [(3, 16, 16, 1, 8, 8), (2, 5, 7, 2, 2, 3),
+                                  (4, 6, 9, 3, 4, 2), (1, 12, 10, 1, 8, 16)])
+def test_slots_match_constructive_enumeration(dims):
+    lay = orc.Layout(*dims)
+    src = _enumerate_window_order(lay)
+    slot = orc.slot_of_token(lay)
+    assert len(src) == orc.sizes(lay)["Np"]
+    for p, n in enumerate(src):
+        if n >= 0:
+            assert slot[n] == p
+    assert sorted(n for n in src if n >= 0) == list(range(lay.T * lay.H * lay.W))
+
+
+def test_whole_frame_windows_are_identity():
+    for lay in (orc.Layout(3, 4, 5, 1, 4, 5), orc.Layout(2, 3, 8, 1, 1, 8)):
+        assert (orc.slot_of_token(lay) == np.arange(lay.T * lay.H * lay.W)).all()
+
+
+@settings(max_examples=60, deadline=None)
+@given(T=st.integers(1, 5), H=st.integers(1, 9), W=st.integers(1, 9),
+       wt=st.integers(1, 3), wh=st.integers(1, 4), ww=st.integers(1, 4),
+       n_text=st.integers(0, 7), permute=st.integers(0, 1))
+def test_permutation_is_a_bijection_and_roundtrips(T, H, W, wt, wh, ww, n_text,
+                                                   permute):
+    lay = orc.Layout(T, H, W, wt, wh, ww, n_text=n_text, permute=permute)
+    z = orc.sizes(lay)
+    slot = orc.slot_of_token(lay)
+    assert len(np.unique(slot)) == z["N"]
+    assert slot.min() >= 0 and slot.max() < z["Np"]
+    assert z["Np"] % z["bs"] == 0 and z["Np"] >= z["N"]
+    x = _rng(7).standard_normal((1, 2, z["L"], 3))
+    xp = orc.permute(x, lay)
+    assert xp.shape == (1, 2, z["Lp"], 3)
+    assert (xp[..., ~orc.slot_valid(lay), :] == 0).all()
+    assert np.array_equal(orc.unpermute(xp, lay), x)
+    assert np.array_equal(np.sort(xp[0, 0, orc.slot_valid(lay), 0]),
+                          np.sort(x[0, 0, :, 0]))
+    counts = orc.block_counts(lay)
+    assert counts.sum() == z["N"] and (counts >= 1).all()
+
+
+def test_raster_mode_sizes_and_sink():
+    # 21x45x80 raster with 128-token blocks: 591 blocks, last one 80 valid,
+    # frame 0 (3600 tokens) touches 29 blocks.
+    lay = orc.Layout(21, 45, 80, 2, 8, 8, permute=0, sink=1)
+    z = orc.sizes(lay)
+    assert (z["nb"], z["Np"]) == (591, 75648)
+    assert orc.block_counts(lay)[-1] == 80
+    assert orc.sink_blocks(lay).tolist() == list(range(29))
+
+
+def test_video720_padding_profile():
+    lay = orc.Layout(21, 45, 80, 2, 8, 8, sink=1)
+    z = orc.sizes(lay)
+    assert (z["Np"], z["nb"]) == (84480, 660)
+    c = orc.block_counts(lay)
+    assert {v: int((c == v).sum()) for v in np.unique(c)} == \
+        {40: 10, 64: 50, 80: 100, 128: 500}
+    assert len(orc.sink_blocks(lay)) == 60
+
+
+# ---------------------------------------------------------------- block means
+
+@pytest.mark.parametrize("dims", [(3, 16, 16, 1, 8, 8), (5, 7, 9, 2, 4, 4),
+                                  (3, 5, 6, 2, 2, 4)])
+def test_means_of_affine_field_are_centroids(dims):
+    """x(t,h,w) = a + bt t + bh h + bw w  =>  block mean = x(centroid of the
+    block's valid tokens); the valid set is a box, so the centroid is the
+    midpoint of each clipped range."""
+    lay = orc.Layout(*dims)
+    T, H, W, wt, wh, ww = dims
+    d = 5
+    r = _rng(3)
+    a, bt, bh, bw = (r.standard_normal(d) for _ in range(4))
+    t, h, w = np.meshgrid(np.arange(T), np.arange(H), np.arange(W),
+                          indexing="ij")
+    x = (a + bt * t[..., None] + bh * h[..., None] + bw * w[..., None])
+    x = x.reshape(1, 1, T * H * W, d)
+    means = orc.block_means(orc.permute(x, lay), lay)[0, 0]
+    z = orc.sizes(lay)
+    mid = lambda b, win, n: (b * win + min((b + 1) * win, n) - 1) / 2.0
+    for B in range(z["nb"]):
+        ib, jw = divmod(B, z["nW"])
+        it, ih = divmod(ib, z["nH"])
+        want = (a + bt * mid(it, wt, T) + bh * mid(ih, wh, H)
+                + bw * mid(jw, ww, W))
+        np.testing.assert_allclose(means[B], want, rtol=0, atol=1e-12)
+
+
+def test_means_ignore_pad_slots_and_constants():
+    lay = orc.Layout(3, 5, 6, 2, 2, 4)
+    z = orc.sizes(lay)
+    x = np.full((1, 2, z["L"], 4), 2.5)
+    xp = orc.permute(x, lay)
+    np.testing.assert_allclose(orc.block_means(xp, lay), 2.5, atol=1e-15)
+    y = _rng(5).standard_normal((1, 2, z["L"], 4))
+    yp = orc.permute(y, lay)
+    poisoned = yp.copy()
+    poisoned[..., ~orc.slot_valid(lay), :] = 1e6
+    assert np.array_equal(orc.block_means(poisoned, lay),
+                          orc.block_means(yp, lay))
+
+
+def test_means_by_brute_force():
+    lay = orc.Layout(3, 5, 6, 2, 2, 4)
+    z = orc.sizes(lay)
+    x = _rng(11).standard_normal((1, 1, z["L"], 3))
+    means = orc.block_means(orc.permute(x, lay), lay)[0, 0]
+    for B in range(z["nb"]):
+        members = [n for n in range(z["N"])
+                   if orc.slot_of_token(lay)[n] // z["bs"] == B]
+        np.testing.assert_allclose(means[B], x[0, 0, members].mean(axis=0),
+                                   atol=1e-14)
+
+
+# ---------------------------------------------------------------- mask rule
+
+def test_block_scores_softmax():
+    r = _rng(2)
+    qbar, kbar = r.standard_normal((1, 2, 7, 16)), r.standard_normal((1, 2, 7, 16))
+    l, P = orc.block_scores(qbar, kbar)
+    np.testing.assert_allclose(P.sum(-1), 1.0, atol=1e-14)
+    ref = scipy.special.softmax(np.einsum("bhid,bhjd->bhij", qbar, kbar) / 4.0,
+                                axis=-1)
+    np.testing.assert_allclose(P, ref, atol=1e-14)
+    np.testing.assert_allclose(l[0, 1, 3, 5], qbar[0, 1, 3] @ kbar[0, 1, 5] / 4.0,
+                               atol=1e-14)
+
+
+def test_keep_counts_golden():
+    with open(os.path.join(GOLDEN, "keep_counts.txt")) as f:
+        rows = [list(map(int, l.split())) for l in f
+                if l.strip() and not l.startswith("#")]
+    for n, s, ns, k, keff in rows:
+        assert orc.keep_count(n, s, ns) == (k, keff), (n, s, ns)
+
+
+@pytest.mark.parametrize("n", [1, 7, 12, 32, 591, 660, 960])
+def test_kept_fraction_hits_target(n):
+    for s in range(0, 100):
+        k, _ = orc.keep_count(n, s, 0)
+        assert abs(k / n - (1 - s / 100)) <= 1 / (2 * n) + 1e-12
+
+
+def _planted(lay, values, d=8):
+    """Tokens whose key-block means are values[j] * e0 and whose query means
+    are e0, so l_ij = values[j] / sqrt(d) exactly (up to rounding)."""
+    z = orc.sizes(lay)
+    slot = orc.slot_of_token(lay)
+    blk = slot // z["bs"]
+    k = np.zeros((1, 1, z["L"], d))
+    k[0, 0, :z["N"], 0] = values[blk]
+    q = np.zeros((1, 1, z["L"], d))
+    q[0, 0, :, 0] = 1.0
+    return q, k
+
+
+def test_planted_ranking_gives_expected_mask():
+    lay = orc.Layout(2, 8, 12, 1, 4, 4, sink=1)
+    z = orc.sizes(lay)
+    nb = z["nb"]
+    assert nb == 12
+    values = _rng(9).permutation(nb).astype(np.float64)
+    q, k = _planted(lay, values)
+    qbar = orc.block_means(orc.permute(q, lay), lay)
+    kbar = orc.block_means(orc.permute(k, lay), lay)
+    sinks = [0, 1, 2, 3, 4, 5]
+    for s in (0, 25, 50, 75, 95):
+        kept, _ = orc.predict_mask(qbar, kbar, lay, s)
+        _, keff = orc.keep_count(nb, s, len(sinks))
+        others = sorted((j for j in range(nb) if j not in sinks),
+                        key=lambda j: -values[j])
+        want = sorted(sinks + others[:keff - len(sinks)])
+        for row in kept[0][0]:
+            assert row.tolist() == want
+
+
+def test_ties_go_to_lower_index_and_sinks_only_when_budget_is_small():
+    lay = orc.Layout(2, 8, 12, 1, 4, 4, sink=1)
+    q, k = _planted(lay, np.ones(12))
+    qbar = orc.block_means(orc.permute(q, lay), lay)
+    kbar = orc.block_means(orc.permute(k, lay), lay)
+    kept, _ = orc.predict_mask(qbar, kbar, lay, 50)
+    assert kept[0][0][0].tolist() == [0, 1, 2, 3, 4, 5]          # k_eff = 6
+    kept, _ = orc.predict_mask(qbar, kbar, lay, 25)
+    assert kept[0][0][0].tolist() == list(range(9))              # 6 sinks + 6,7,8
+    kept, _ = orc.predict_mask(qbar, kbar, lay, 90)
+    assert kept[0][0][0].tolist() == [0, 1, 2, 3, 4, 5]          # sink-bound
+
+
+def test_mask_by_brute_force_subset_search():
+    """With distinct scores, the kept non-sink set is the unique k-subset of
+    non-sink blocks with the largest logit sum."""
+    lay = orc.Layout(3, 4, 6, 1, 2, 3, sink=1)       # 12 blocks, 4 sinks
+    z = orc.sizes(lay)
+    r = _rng(21)
+    q = r.standard_normal((1, 2, z["L"], 6))
+    k = r.standard_normal((1, 2, z["L"], 6))
+    qbar = orc.block_means(orc.permute(q, lay), lay)
+    kbar = orc.block_means(orc.permute(k, lay), lay)
+    sinks = orc.sink_blocks(lay).tolist()
+    assert sinks == [0, 1, 2, 3]
+    for s in (30, 60):
+        kept, l = orc.predict_mask(qbar, kbar, lay, s)
+        _, keff = orc.keep_count(12, s, 4)
+        for h in range(2):
+            for i in range(12):
+                logits = qbar[0, h, i] @ kbar[0, h].T / math.sqrt(6)
+                best = max(itertools.combinations(range(4, 12), keff - 4),
+                           key=lambda c: sum(logits[j] for j in c))
+                assert kept[0][h][i].tolist() == sorted(sinks + list(best))
+
+
+def test_text_tiles_join_every_row():
+    lay = orc.Layout(2, 4, 4, 1, 2, 2, n_text=6, sink=1)
+    z = orc.sizes(lay)
+    assert (z["nb"], z["n_text_tiles"]) == (8, 2)
+    r = _rng(4)
+    qbar = r.standard_normal((1, 1, 8, 4))
+    kbar = r.standard_normal((1, 1, 8, 4))
+    kept, _ = orc.predict_mask(qbar, kbar, lay, 50)
+    rows = kept[0][0]
+    assert len(rows) == 10
+    for row in rows[:8]:
+        assert row[-2:].tolist() == [8, 9] and len(row) == 4 + 2
+        assert set([0, 1, 2, 3]) <= set(row.tolist())
+    for row in rows[8:]:
+        assert row.tolist() == list(range(10))
+
+
+# ---------------------------------------------------------------- attention
+
+def _dense_attention(q, k, v):
+    """Textbook softmax(q k^T / sqrt(d)) v in fp64 (RainFusion page review,
+    Assumptions, Eq. (1)), written independently of the oracle."""
+    s = np.einsum("bhid,bhjd->bhij", q, k) / math.sqrt(q.shape[-1])
+    return np.einsum("bhij,bhjd->bhid", scipy.special.softmax(s, axis=-1), v)
+
+
+@pytest.mark.parametrize("dims,n_text,permute", [((3, 16, 16, 1, 8, 8), 0, 1),
+                                                 ((3, 5, 7, 2, 2, 4), 0, 1),
+                                                 ((2, 6, 6, 1, 4, 4), 5, 1),
+                                                 ((3, 5, 7, 2, 2, 4), 3, 0)])
+def test_zero_sparsity_equals_dense_attention(dims, n_text, permute):
+    lay = orc.Layout(*dims, n_text=n_text, permute=permute, sink=1)
+    z = orc.sizes(lay)
+    r = _rng(13)
+    q, k, v = (r.standard_normal((1, 2, z["L"], 8)) for _ in range(3))
+    res = orc.run(q, k, v, lay, 0)
+    np.testing.assert_allclose(res["o"], _dense_attention(q, k, v),
+                               rtol=0, atol=1e-12)
+
+
+def test_constant_values_give_constant_output():
+    lay = orc.Layout(3, 5, 7, 2, 2, 4, sink=1)
+    z = orc.sizes(lay)
+    r = _rng(17)
+    q, k = (r.standard_normal((1, 1, z["L"], 4)) for _ in range(2))
+    v = np.tile(np.array([1.5, -2.0, 0.25, 3.0]), (1, 1, z["L"], 1))
+    o = orc.run(q, k, v, lay, 70)["o"]
+    np.testing.assert_allclose(o, v, atol=1e-13)
+
+
+def _token_block(lay, z):
+    """Block of each raster token from its coordinates (brute force)."""
+    out = []
+    for t in range(lay.T):
+        for h in range(lay.H):
+            for w in range(lay.W):
+                if lay.permute:
+                    out.append(((t // lay.wt) * z["nH"] + h // lay.wh) * z["nW"]
+                               + w // lay.ww)
+                else:
+                    out.append(((t * lay.H + h) * lay.W + w) // z["bs"])
+    out += [z["nb"] + j // z["bs"] for j in range(lay.n_text)]
+    return np.array(out)
+
+
+@pytest.mark.parametrize("permute,n_text", [(1, 0), (1, 5), (0, 3)])
+def test_sparse_attention_equals_masked_dense_attention(permute, n_text):
+    """Arbitrary kept lists: the permuted-path output, unpermuted, equals
+    dense attention in raster order under the pulled-back token mask."""
+    lay = orc.Layout(3, 5, 7, 2, 2, 4, n_text=n_text, permute=permute)
+    z = orc.sizes(lay)
+    r = _rng(19)
+    q, k, v = (r.standard_normal((1, 1, z["L"], 8)) for _ in range(3))
+    nt = z["n_tiles"]
+    kept = [[[np.sort(r.choice(nt, size=r.integers(1, nt + 1), replace=False))
+              for _ in range(nt)]]]
+    op = orc.sparse_attention(orc.permute(q, lay), orc.permute(k, lay),
+                              orc.permute(v, lay), kept, lay)
+    o = orc.unpermute(op, lay)
+    blk = _token_block(lay, z)
+    allowed = np.array([[blk[j] in set(kept[0][0][blk[i]].tolist())
+                         for j in range(z["L"])] for i in range(z["L"])])
+    s = q[0, 0] @ k[0, 0].T / math.sqrt(8)
+    s[~allowed] = -np.inf
+    want = scipy.special.softmax(s, axis=-1) @ v[0, 0]
+    np.testing.assert_allclose(o[0, 0], want, atol=1e-12)
+    assert (op[0, 0, ~orc.slot_valid(lay)] == 0).all()
+
+
+def test_single_kept_tile_restricts_attention():
+    lay = orc.Layout(2, 8, 8, 1, 4, 4)
+    z = orc.sizes(lay)
+    r = _rng(23)
+    q, k, v = (r.standard_normal((1, 1, z["L"], 4)) for _ in range(3))
+    kept = [[[np.array([5]) for _ in range(z["n_tiles"])]]]
+    qp, kp, vp = (orc.permute(x, lay) for x in (q, k, v))
+    op = orc.sparse_attention(qp, kp, vp, kept, lay)
+    members = [n for n in range(z["N"]) if _token_block(lay, z)[n] == 5]
+    want = _dense_attention(q, k[:, :, members], v[:, :, members])
+    np.testing.assert_allclose(orc.unpermute(op, lay), want, atol=1e-12)
+
+
+def test_query_tile_subset_marks_the_rest_nan():
+    lay = orc.Layout(2, 8, 8, 1, 4, 4)
+    z = orc.sizes(lay)
+    r = _rng(29)
+    q, k, v = (orc.permute(r.standard_normal((1, 1, z["L"], 4)), lay)
+               for _ in range(3))
+    kept = [[[np.arange(z["n_tiles"]) for _ in range(z["n_tiles"])]]]
+    part = orc.sparse_attention(q, k, v, kept, lay, query_tiles={(0, 0): [2]})
+    full = orc.sparse_attention(q, k, v, kept, lay)
+    bs = z["bs"]
+    assert np.array_equal(part[0, 0, 2 * bs:3 * bs], full[0, 0, 2 * bs:3 * bs])
+    assert np.isnan(part[0, 0, :2 * bs]).all()
