@@ -1,0 +1,195 @@
+// Online sparse-mask prediction from the block representative tokens
+// (RainFusion2.0 page, Abstract key insights (1) mean tokens for sparse mask
+// prediction and (3) first-frame sink; TL;DR).
+//
+// For query block i of head (b, h): logits l_ij = qbar_i . kbar_j / sqrt(d)
+// over the video key blocks, keep the sink blocks plus the k_eff - n_sink
+// highest non-sink logits (ties to the lower block index), then every text
+// tile.  The row softmax is monotone, so ranking by the raw fp32 dot product
+// is ranking by the softmax score.
+//
+// One workgroup serves R query rows of one head:
+//   1. the R rows of qbar go to LDS; each thread owns key blocks j and
+//      accumulates R dot products in fp32 (kbar_j streamed once per R rows,
+//      qbar read by LDS broadcast); the R x nb dots stay in LDS;
+//   2. each wave selects for its rows: an exact k-th-largest search over the
+//      order-preserving integer image of the fp32 dots (32 bisection steps of
+//      wave-wide ballots), then an ascending ballot/prefix-count compaction
+//      that also breaks ties by index.  No atomics: the result is bitwise
+//      deterministic.
+#include "rf_internal.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+__device__ inline uint32_t order_key(float f) {
+  if (f == 0.f) f = 0.f;  // -0 and +0 rank equal
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ inline int popc64(uint64_t m) { return __popcll(m); }
+
+template <int D, int R>
+__global__ __launch_bounds__(kThreads) void predict_mask_kernel(
+    const float* __restrict__ qbar, const float* __restrict__ kbar,
+    const uint8_t* __restrict__ is_sink, int32_t* __restrict__ kept,
+    float* __restrict__ logits, int32_t nb, int32_t n_sink, int32_t k_eff,
+    int32_t n_tt, int32_t row_len, int64_t nnz, float scale) {
+  extern __shared__ float smem[];
+  float* qs = smem;            // [R][D]
+  float* sc = smem + R * D;    // [R][nb]
+  const int64_t bh = blockIdx.y;
+  const int i0 = blockIdx.x * R;
+  const float* qh = qbar + bh * nb * D;
+  const float* kh = kbar + bh * nb * D;
+  for (int t = threadIdx.x; t < R * D; t += kThreads) {
+    const int r = t / D;
+    qs[t] = (i0 + r < nb) ? qh[int64_t(i0 + r) * D + t % D] : 0.f;
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < nb; j += kThreads) {
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.f;
+    const float4* kr = reinterpret_cast<const float4*>(kh + int64_t(j) * D);
+#pragma unroll 4
+    for (int c = 0; c < D / 4; ++c) {
+      const float4 kv = kr[c];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float4 qv = reinterpret_cast<const float4*>(qs + r * D)[c];
+        acc[r] = fmaf(kv.x, qv.x, acc[r]);
+        acc[r] = fmaf(kv.y, qv.y, acc[r]);
+        acc[r] = fmaf(kv.z, qv.z, acc[r]);
+        acc[r] = fmaf(kv.w, qv.w, acc[r]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      sc[r * nb + j] = acc[r];
+      if (logits != nullptr && i0 + r < nb)
+        logits[(bh * nb + i0 + r) * nb + j] = acc[r] * scale;
+    }
+  }
+  __syncthreads();
+
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int k_sel = k_eff - n_sink;
+  const int M = (nb + 63) / 64;
+  for (int r = wave; r < R; r += kWaves) {
+    const int i = i0 + r;
+    if (i >= nb) break;
+    const float* row = sc + r * nb;
+    // Bisection for tau = the k_sel-th largest key among non-sink blocks.
+    uint32_t tau = 0;
+    if (k_sel > 0) {
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t t = tau | (1u << bit);
+        int cnt = 0;
+        for (int m = 0; m < M; ++m) {
+          const int j = lane + 64 * m;
+          const bool ge = j < nb && !is_sink[j] && order_key(row[j]) >= t;
+          cnt += popc64(__ballot(ge));
+        }
+        if (cnt >= k_sel) tau = t;
+      }
+    }
+    // Keys above tau are kept; among keys equal to tau the lowest indices
+    // fill the remaining places.
+    int n_gt = 0;
+    if (k_sel > 0) {
+      for (int m = 0; m < M; ++m) {
+        const int j = lane + 64 * m;
+        n_gt += popc64(__ballot(j < nb && !is_sink[j] && order_key(row[j]) > tau));
+      }
+    }
+    const int n_eq_take = k_sel - n_gt;
+    int32_t* out = kept + bh * nnz + int64_t(i) * row_len;
+    int pos = 0, eq_seen = 0;
+    for (int m = 0; m < M; ++m) {
+      const int j = lane + 64 * m;
+      bool keep = false, eq = false;
+      if (j < nb) {
+        if (is_sink[j]) {
+          keep = true;
+        } else if (k_sel > 0) {
+          const uint32_t key = order_key(row[j]);
+          keep = key > tau;
+          eq = key == tau;
+        }
+      }
+      const uint64_t eqm = __ballot(eq);
+      if (eq && eq_seen + popc64(eqm & lt_mask) < n_eq_take) keep = true;
+      eq_seen += popc64(eqm);
+      const uint64_t km = __ballot(keep);
+      if (keep) out[pos + popc64(km & lt_mask)] = j;
+      pos += popc64(km);
+    }
+    for (int t = lane; t < n_tt; t += 64) out[pos + t] = nb + t;
+  }
+}
+
+// Text query tiles attend to every tile.
+__global__ void text_rows_kernel(int32_t* __restrict__ kept, int32_t nb,
+                                 int32_t n_tiles, int32_t row_len_video,
+                                 int64_t nnz) {
+  const int64_t bh = blockIdx.y;
+  int32_t* out = kept + bh * nnz + int64_t(nb) * row_len_video +
+                 int64_t(blockIdx.x) * n_tiles;
+  for (int t = threadIdx.x; t < n_tiles; t += blockDim.x) out[t] = t;
+}
+
+template <int D, int R>
+void launch(const rf_plan* p, const float* qbar, const float* kbar,
+            int32_t* kept, float* logits, int BH, const rf_keep& kc,
+            hipStream_t st) {
+  const int nb = p->sz.nb;
+  const size_t lds = sizeof(float) * (size_t(R) * D + size_t(R) * nb);
+  dim3 grid((nb + R - 1) / R, BH);
+  hipLaunchKernelGGL((predict_mask_kernel<D, R>), grid, dim3(kThreads), lds, st,
+                     qbar, kbar, p->is_sink, kept, logits, nb, p->sz.n_sink,
+                     kc.k_eff, p->sz.n_text_tiles, kc.row_len_video,
+                     kc.nnz_per_head, 1.0f / sqrtf(float(D)));
+}
+
+}  // namespace
+
+extern "C" rf_status rf_predict_mask(const rf_plan* plan, const float* qbar,
+                                     const float* kbar, int32_t B, int32_t H,
+                                     int32_t d, int32_t sparsity_pct,
+                                     int32_t* kept_idx, float* logits_or_null,
+                                     hipStream_t stream) {
+  rf_status st = rf::check_call(plan, B, H, d, RF_F32, "rf_predict_mask");
+  if (st != RF_OK) return st;
+  if (!rf::aligned16(qbar) || !rf::aligned16(kbar) || !rf::aligned16(kept_idx))
+    return rf::fail(RF_ERR_INVALID_ARG, "rf_predict_mask: null or misaligned buffer");
+  if (logits_or_null != nullptr && !rf::aligned16(logits_or_null))
+    return rf::fail(RF_ERR_INVALID_ARG, "rf_predict_mask: misaligned logits");
+  rf_keep kc;
+  st = rf_keep_count(&plan->lay, sparsity_pct, &kc);
+  if (st != RF_OK) return st;
+  const int nb = plan->sz.nb;
+  // Dots of R rows x nb blocks must fit in LDS next to the R query rows.
+  const size_t budget = 128 * 1024;
+  const int BH = B * H;
+  if (sizeof(float) * 16 * (size_t(nb) + d) <= budget) {
+    if (d == 128) launch<128, 16>(plan, qbar, kbar, kept_idx, logits_or_null, BH, kc, stream);
+    else launch<64, 16>(plan, qbar, kbar, kept_idx, logits_or_null, BH, kc, stream);
+  } else if (sizeof(float) * 4 * (size_t(nb) + d) <= budget) {
+    if (d == 128) launch<128, 4>(plan, qbar, kbar, kept_idx, logits_or_null, BH, kc, stream);
+    else launch<64, 4>(plan, qbar, kbar, kept_idx, logits_or_null, BH, kc, stream);
+  } else {
+    return rf::fail(RF_ERR_UNSUPPORTED, "rf_predict_mask: %d blocks per row "
+                    "exceed the LDS budget", nb);
+  }
+  if (plan->sz.n_text_tiles > 0) {
+    dim3 grid(plan->sz.n_text_tiles, BH);
+    hipLaunchKernelGGL(text_rows_kernel, grid, dim3(256), 0, stream, kept_idx,
+                       nb, plan->sz.n_tiles, kc.row_len_video, kc.nnz_per_head);
+  }
+  return rf::check_launch("rf_predict_mask");
+}

@@ -1,0 +1,192 @@
+// 3D window permutation and its inverse (RainFusion2.0 page, Abstract key
+// insight (2) "spatiotemporal-aware token permutation"; TL;DR "3D window
+// permutation"; Figure 3 shows the artifacts it removes at 80% sparsity).
+//
+// Pure data movement, bound by HBM bandwidth.  Every thread moves 16-byte
+// chunks; the gather side reads whole window rows (ww tokens contiguous in
+// raster order), the write side is fully contiguous.  The slot -> token map
+// comes from the plan, so the kernels hold no index arithmetic of their own.
+#include "rf_internal.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kChunksPerThread = 4;
+
+// xp[bh][s][:] = x[bh][slot_src[s]][:] (zeros for pad).  Grid: x over the
+// chunks of one (b, h), y over b*H + h.
+__global__ __launch_bounds__(kThreads) void permute_rows_kernel(
+    const uint4* __restrict__ x, uint4* __restrict__ xp,
+    const int32_t* __restrict__ slot_src, int32_t cpr, int64_t L, int64_t Lp) {
+  const int64_t bh = blockIdx.y;
+  const int32_t per_head = int32_t(Lp) * cpr;
+  const uint4* src = x + bh * L * cpr;
+  uint4* dst = xp + bh * Lp * cpr;
+  const int32_t base = blockIdx.x * (kThreads * kChunksPerThread) + threadIdx.x;
+  uint4 v[kChunksPerThread];
+#pragma unroll
+  for (int u = 0; u < kChunksPerThread; ++u) {
+    const int32_t c = base + u * kThreads;
+    v[u] = make_uint4(0, 0, 0, 0);
+    if (c < per_head) {
+      const int32_t s = c / cpr;
+      const int32_t tok = slot_src[s];
+      if (tok >= 0) v[u] = src[int64_t(tok) * cpr + (c - s * cpr)];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kChunksPerThread; ++u) {
+    const int32_t c = base + u * kThreads;
+    if (c < per_head) dst[c] = v[u];
+  }
+}
+
+// x[bh][n][:] = xp[bh][tok_slot[n]][:].
+__global__ __launch_bounds__(kThreads) void unpermute_rows_kernel(
+    const uint4* __restrict__ xp, uint4* __restrict__ x,
+    const int32_t* __restrict__ tok_slot, int32_t cpr, int64_t L, int64_t Lp) {
+  const int64_t bh = blockIdx.y;
+  const int32_t per_head = int32_t(L) * cpr;
+  const uint4* src = xp + bh * Lp * cpr;
+  uint4* dst = x + bh * L * cpr;
+  const int32_t base = blockIdx.x * (kThreads * kChunksPerThread) + threadIdx.x;
+  uint4 v[kChunksPerThread];
+#pragma unroll
+  for (int u = 0; u < kChunksPerThread; ++u) {
+    const int32_t c = base + u * kThreads;
+    if (c < per_head) {
+      const int32_t n = c / cpr;
+      v[u] = src[int64_t(tok_slot[n]) * cpr + (c - n * cpr)];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kChunksPerThread; ++u) {
+    const int32_t c = base + u * kThreads;
+    if (c < per_head) dst[c] = v[u];
+  }
+}
+
+// Tile-transposed permutation: xt[bh][tile][f][s] = x[bh][slot_src[tile*BS+s]][f].
+// One workgroup per (tile, b*H + h).  The tile's BS rows are gathered into
+// LDS (16 lanes per 256-byte row), then each thread transposes one VE x VE
+// sub-block (VE = elements per 16-byte chunk) in registers and writes VE
+// output chunks.  E = element bytes, D = head dim.
+template <int E, int D, int BS>
+__global__ __launch_bounds__(kThreads) void permute_tiles_t_kernel(
+    const uint8_t* __restrict__ x, uint8_t* __restrict__ xt,
+    const int32_t* __restrict__ slot_src, int64_t L, int64_t Lp,
+    int32_t n_tiles) {
+  constexpr int VE = 16 / E;            // elements per chunk
+  constexpr int CPR = D / VE;           // chunks per token row
+  constexpr int ROW = D * E + 16;       // padded LDS row (bytes)
+  __shared__ __align__(16) uint8_t lds[BS * ROW];
+  const int64_t bh = blockIdx.y;
+  const int32_t tile = blockIdx.x;
+  const uint8_t* src = x + bh * L * (D * E);
+  for (int c = threadIdx.x; c < BS * CPR; c += kThreads) {
+    const int s = c / CPR, k = c % CPR;
+    const int64_t slot = int64_t(tile) * BS + s;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (slot < Lp) {
+      const int32_t tok = slot_src[slot];
+      if (tok >= 0)
+        v = *reinterpret_cast<const uint4*>(src + int64_t(tok) * (D * E) + k * 16);
+    }
+    *reinterpret_cast<uint4*>(lds + s * ROW + k * 16) = v;
+  }
+  __syncthreads();
+  // Sub-block (fc, sc): features fc*VE.., slots sc*VE..
+  constexpr int NSUB = CPR * (BS / VE);
+  uint8_t* dst = xt + (bh * n_tiles + tile) * int64_t(D) * BS * E;
+  for (int b = threadIdx.x; b < NSUB; b += kThreads) {
+    const int fc = b % CPR, sc = b / CPR;
+    uint4 rows[VE];
+#pragma unroll
+    for (int e = 0; e < VE; ++e)
+      rows[e] = *reinterpret_cast<const uint4*>(lds + (sc * VE + e) * ROW + fc * 16);
+#pragma unroll
+    for (int f = 0; f < VE; ++f) {
+      uint4 out;
+      if constexpr (E == 2) {
+        uint16_t t[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          t[e] = reinterpret_cast<const uint16_t*>(&rows[e])[f];
+        out = *reinterpret_cast<const uint4*>(t);
+      } else {
+        uint32_t t[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          t[e] = reinterpret_cast<const uint32_t*>(&rows[e])[f];
+        out = *reinterpret_cast<const uint4*>(t);
+      }
+      *reinterpret_cast<uint4*>(dst + (int64_t(fc * VE + f) * BS + sc * VE) * E) = out;
+    }
+  }
+}
+
+template <int E, int D, int BS>
+void launch_tiles_t(const rf_plan* p, const void* x, void* xt, int BH,
+                    hipStream_t st) {
+  dim3 grid(p->sz.n_tiles, BH);
+  hipLaunchKernelGGL((permute_tiles_t_kernel<E, D, BS>), grid, dim3(kThreads),
+                     0, st, static_cast<const uint8_t*>(x),
+                     static_cast<uint8_t*>(xt), p->slot_src, p->sz.L, p->sz.Lp,
+                     p->sz.n_tiles);
+}
+
+}  // namespace
+
+extern "C" {
+
+rf_status rf_permute(const rf_plan* plan, const void* x, void* xp, int32_t B,
+                     int32_t H, int32_t d, rf_dtype dtype, rf_order order,
+                     hipStream_t stream) {
+  rf_status st = rf::check_call(plan, B, H, d, dtype, "rf_permute");
+  if (st != RF_OK) return st;
+  if (!rf::aligned16(x) || !rf::aligned16(xp))
+    return rf::fail(RF_ERR_INVALID_ARG, "rf_permute: null or misaligned buffer");
+  if (order != RF_ROWS && order != RF_TILES_T)
+    return rf::fail(RF_ERR_INVALID_ARG, "rf_permute: unknown order %d", int(order));
+  const int E = rf::esize(dtype);
+  const int cpr = d * E / 16;
+  const int BH = B * H;
+  if (order == RF_ROWS) {
+    const int64_t per_head = plan->sz.Lp * cpr;
+    dim3 grid((per_head + kThreads * kChunksPerThread - 1) /
+                  (kThreads * kChunksPerThread), BH);
+    hipLaunchKernelGGL(permute_rows_kernel, grid, dim3(kThreads), 0, stream,
+                       static_cast<const uint4*>(x), static_cast<uint4*>(xp),
+                       plan->slot_src, cpr, plan->sz.L, plan->sz.Lp);
+  } else {
+    const int bs = plan->sz.bs;
+    if (E == 2 && d == 128 && bs == 128) launch_tiles_t<2, 128, 128>(plan, x, xp, BH, stream);
+    else if (E == 2 && d == 128 && bs == 64) launch_tiles_t<2, 128, 64>(plan, x, xp, BH, stream);
+    else if (E == 2 && d == 64 && bs == 128) launch_tiles_t<2, 64, 128>(plan, x, xp, BH, stream);
+    else if (E == 2 && d == 64 && bs == 64) launch_tiles_t<2, 64, 64>(plan, x, xp, BH, stream);
+    else if (E == 4 && d == 128 && bs == 128) launch_tiles_t<4, 128, 128>(plan, x, xp, BH, stream);
+    else if (E == 4 && d == 128 && bs == 64) launch_tiles_t<4, 128, 64>(plan, x, xp, BH, stream);
+    else if (E == 4 && d == 64 && bs == 128) launch_tiles_t<4, 64, 128>(plan, x, xp, BH, stream);
+    else launch_tiles_t<4, 64, 64>(plan, x, xp, BH, stream);
+  }
+  return rf::check_launch("rf_permute");
+}
+
+rf_status rf_unpermute(const rf_plan* plan, const void* xp, void* x,
+                       int32_t B, int32_t H, int32_t d, rf_dtype dtype,
+                       hipStream_t stream) {
+  rf_status st = rf::check_call(plan, B, H, d, dtype, "rf_unpermute");
+  if (st != RF_OK) return st;
+  if (!rf::aligned16(x) || !rf::aligned16(xp))
+    return rf::fail(RF_ERR_INVALID_ARG, "rf_unpermute: null or misaligned buffer");
+  const int cpr = d * rf::esize(dtype) / 16;
+  const int64_t per_head = plan->sz.L * cpr;
+  dim3 grid((per_head + kThreads * kChunksPerThread - 1) /
+                (kThreads * kChunksPerThread), B * H);
+  hipLaunchKernelGGL(unpermute_rows_kernel, grid, dim3(kThreads), 0, stream,
+                     static_cast<const uint4*>(xp), static_cast<uint4*>(x),
+                     plan->tok_slot, cpr, plan->sz.L, plan->sz.Lp);
+  return rf::check_launch("rf_unpermute");
+}
+
+}  // extern "C"

@@ -1,0 +1,305 @@
+"""Python binding of librf.so (ctypes).  Argument marshalling only: every step
+of the path runs in the library's HIP kernels.  Output tensors are
+allocated with torch (device memory plumbing) and handed to the library as
+raw pointers together with torch's current HIP stream.
+
+The library must have been built (``python -m image_diffusion_dits_amd.build``);
+loading fails loudly when it is missing.  There is no fallback path.
+"""
+import ctypes
+import math
+import os
+
+import numpy as np
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librf.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_BUFFER_TOO_SMALL = range(5)
+F32, BF16 = 0, 1
+ROWS, TILES_T = 0, 1
+
+_c_i32, _c_i64, _c_f32, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [(n, _c_i32) for n in
+                ("T", "H", "W", "wt", "wh", "ww", "n_text", "permute", "sink")]
+
+
+class Sizes(ctypes.Structure):
+    _fields_ = [("N", _c_i64), ("Np", _c_i64), ("L", _c_i64), ("Lp", _c_i64),
+                ("bs", _c_i32), ("nb", _c_i32), ("n_text_tiles", _c_i32),
+                ("n_tiles", _c_i32), ("n_sink", _c_i32)]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+class Keep(ctypes.Structure):
+    _fields_ = [("k", _c_i32), ("k_eff", _c_i32), ("row_len_video", _c_i32),
+                ("row_len_text", _c_i32), ("nnz_per_head", _c_i64)]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+class RfError(RuntimeError):
+    def __init__(self, status, fn, msg):
+        super().__init__(f"{fn}: {msg} (status {status})")
+        self.status = status
+
+
+_P = ctypes.POINTER
+_SIGNATURES = {
+    "rf_layout_sizes": [_P(Layout), _P(Sizes)],
+    "rf_layout_tables": [_P(Layout), _vp, _c_i64, _vp, _c_i64, _vp, _c_i64,
+                         _vp, _c_i64],
+    "rf_keep_count": [_P(Layout), _c_i32, _P(Keep)],
+    "rf_plan_create": [_P(Layout), _P(_vp)],
+    "rf_plan_sizes": [_vp, _P(Sizes)],
+    "rf_permute": [_vp, _vp, _vp, _c_i32, _c_i32, _c_i32, ctypes.c_int,
+                   ctypes.c_int, _vp],
+    "rf_unpermute": [_vp, _vp, _vp, _c_i32, _c_i32, _c_i32, ctypes.c_int, _vp],
+    "rf_block_means": [_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32,
+                       ctypes.c_int, _vp],
+    "rf_predict_mask": [_vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _vp,
+                        _vp, _vp],
+    "rf_sparse_attn": [_vp, _vp, _vp, _vp, _vp, _c_i32, _vp, _c_i32, _c_i32,
+                       _c_i32, _c_f32, ctypes.c_int, _vp],
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m image_diffusion_dits_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGNATURES.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        L.rf_plan_destroy.argtypes = [_vp]
+        L.rf_plan_destroy.restype = None
+        L.rf_status_str.argtypes = [ctypes.c_int]
+        L.rf_status_str.restype = ctypes.c_char_p
+        L.rf_last_error.argtypes = []
+        L.rf_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status, fn):
+    if status != OK:
+        raise RfError(status, fn, lib().rf_last_error().decode())
+
+
+def make_layout(T, H, W, wt, wh, ww, n_text=0, permute=1, sink=0):
+    return Layout(T, H, W, wt, wh, ww, n_text, permute, sink)
+
+
+def _as_layout(lay):
+    if isinstance(lay, Layout):
+        return lay
+    if isinstance(lay, dict):
+        return make_layout(**lay)
+    return make_layout(*lay)
+
+
+# ---------------------------------------------------------------- host helpers
+
+def layout_sizes(lay):
+    out = Sizes()
+    _check(lib().rf_layout_sizes(ctypes.byref(_as_layout(lay)), ctypes.byref(out)),
+           "rf_layout_sizes")
+    return out.as_dict()
+
+
+def layout_tables(lay):
+    """(slot_src, tok_slot, tile_count, is_sink) as numpy arrays."""
+    lay = _as_layout(lay)
+    z = layout_sizes(lay)
+    slot_src = np.empty(z["Lp"], np.int32)
+    tok_slot = np.empty(z["L"], np.int32)
+    count = np.empty(z["n_tiles"], np.int32)
+    sink = np.empty(z["nb"], np.uint8)
+    _check(lib().rf_layout_tables(
+        ctypes.byref(lay), slot_src.ctypes.data, slot_src.size,
+        tok_slot.ctypes.data, tok_slot.size, count.ctypes.data, count.size,
+        sink.ctypes.data, sink.size), "rf_layout_tables")
+    return slot_src, tok_slot, count, sink
+
+
+def keep_count(lay, sparsity_pct):
+    out = Keep()
+    _check(lib().rf_keep_count(ctypes.byref(_as_layout(lay)), int(sparsity_pct),
+                               ctypes.byref(out)), "rf_keep_count")
+    return out.as_dict()
+
+
+# ---------------------------------------------------------------- plan
+
+class Plan:
+    """Device index tables of one layout (rf_plan_create / rf_plan_destroy)."""
+
+    def __init__(self, lay):
+        self.layout = _as_layout(lay)
+        h = _vp()
+        _check(lib().rf_plan_create(ctypes.byref(self.layout), ctypes.byref(h)),
+               "rf_plan_create")
+        self._h = h
+        s = Sizes()
+        _check(lib().rf_plan_sizes(h, ctypes.byref(s)), "rf_plan_sizes")
+        self.sizes = s.as_dict()
+
+    @property
+    def handle(self):
+        return self._h
+
+    def keep(self, sparsity_pct):
+        return keep_count(self.layout, sparsity_pct)
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().rf_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ---------------------------------------------------------------- hot path
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream():
+    return _vp(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return _vp(t.data_ptr())
+
+
+def _bhd(x):
+    if x.dim() != 4 or not x.is_contiguous() or not x.is_cuda:
+        raise ValueError("expected a contiguous CUDA tensor [B, H, tokens, d]")
+    return x.shape[0], x.shape[1], x.shape[3]
+
+
+def permute(plan, x, order=ROWS, out=None):
+    B, H, d = _bhd(x)
+    z = plan.sizes
+    if x.shape[2] != z["L"]:
+        raise ValueError(f"x has {x.shape[2]} tokens, layout needs {z['L']}")
+    if out is None:
+        if order == ROWS:
+            out = torch.empty(B, H, z["Lp"], d, dtype=x.dtype, device=x.device)
+        else:
+            out = torch.empty(B, H, z["n_tiles"], d, z["bs"], dtype=x.dtype,
+                              device=x.device)
+    _check(lib().rf_permute(plan.handle, _ptr(x), _ptr(out), B, H, d,
+                            _dtype_code(x), order, _stream()), "rf_permute")
+    return out
+
+
+def unpermute(plan, xp, out=None):
+    B, H, d = _bhd(xp)
+    z = plan.sizes
+    if xp.shape[2] != z["Lp"]:
+        raise ValueError(f"xp has {xp.shape[2]} slots, layout needs {z['Lp']}")
+    if out is None:
+        out = torch.empty(B, H, z["L"], d, dtype=xp.dtype, device=xp.device)
+    _check(lib().rf_unpermute(plan.handle, _ptr(xp), _ptr(out), B, H, d,
+                              _dtype_code(xp), _stream()), "rf_unpermute")
+    return out
+
+
+def block_means(plan, qp, kp, qbar=None, kbar=None):
+    B, H, d = _bhd(qp)
+    nb = plan.sizes["nb"]
+    if qbar is None:
+        qbar = torch.empty(B, H, nb, d, dtype=torch.float32, device=qp.device)
+    if kbar is None:
+        kbar = torch.empty_like(qbar)
+    _check(lib().rf_block_means(plan.handle, _ptr(qp), _ptr(kp), _ptr(qbar),
+                                _ptr(kbar), B, H, d, _dtype_code(qp), _stream()),
+           "rf_block_means")
+    return qbar, kbar
+
+
+def predict_mask(plan, qbar, kbar, sparsity_pct, kept=None, logits=False):
+    B, H, d = _bhd(qbar)
+    kc = plan.keep(sparsity_pct)
+    if kept is None:
+        kept = torch.empty(B, H, kc["nnz_per_head"], dtype=torch.int32,
+                           device=qbar.device)
+    lg = None
+    if logits:
+        nb = plan.sizes["nb"]
+        lg = torch.empty(B, H, nb, nb, dtype=torch.float32, device=qbar.device)
+    _check(lib().rf_predict_mask(plan.handle, _ptr(qbar), _ptr(kbar), B, H, d,
+                                 int(sparsity_pct), _ptr(kept),
+                                 _ptr(lg) if lg is not None else None,
+                                 _stream()), "rf_predict_mask")
+    return (kept, lg) if logits else kept
+
+
+def sparse_attn(plan, qp, kp, vt, kept, sparsity_pct, scale=None, out=None):
+    B, H, d = _bhd(qp)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(qp)
+    _check(lib().rf_sparse_attn(plan.handle, _ptr(qp), _ptr(kp), _ptr(vt),
+                                _ptr(kept), int(sparsity_pct), _ptr(out), B, H,
+                                d, float(scale), _dtype_code(qp), _stream()),
+           "rf_sparse_attn")
+    return out
+
+
+def kept_rows(plan, kept, sparsity_pct):
+    """Split a flat kept list [B, H, nnz] (on the host) into per-row arrays."""
+    kc = plan.keep(sparsity_pct)
+    z = plan.sizes
+    k = kept.detach().cpu().numpy()
+    rows = []
+    for b in range(k.shape[0]):
+        per_head = []
+        for h in range(k.shape[1]):
+            flat = k[b, h]
+            lv = kc["row_len_video"]
+            r = [flat[i * lv:(i + 1) * lv] for i in range(z["nb"])]
+            base = z["nb"] * lv
+            lt = kc["row_len_text"]
+            r += [flat[base + t * lt: base + (t + 1) * lt]
+                  for t in range(z["n_text_tiles"])]
+            per_head.append(r)
+        rows.append(per_head)
+    return rows
+
+
+def sparse_attention(q, k, v, plan, sparsity_pct, scale=None):
+    """The whole path on raster tensors [B, H, N + n_text, d]: permute,
+    pool, predict, attend, unpermute.  Returns (o, kept)."""
+    qp = permute(plan, q)
+    kp = permute(plan, k)
+    vt = permute(plan, v, order=TILES_T)
+    qbar, kbar = block_means(plan, qp, kp)
+    kept = predict_mask(plan, qbar, kbar, sparsity_pct)
+    op = sparse_attn(plan, qp, kp, vt, kept, sparsity_pct, scale=scale)
+    return unpermute(plan, op), kept

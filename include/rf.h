@@ -1,0 +1,204 @@
+/*
+ * rf.h -- C ABI of the MI355X (gfx950) RainFusion2.0 block-sparse attention
+ * hot path.
+ *
+ * Sources, cited by page title and section:
+ *   [RF2] "RainFusion2.0: Temporal-Spatial Awareness and Hardware-Efficient
+ *         Block-wise Sparse Attention" (arXiv 2512.24086): Abstract key
+ *         insights (1) block-wise mean values as representative tokens for
+ *         sparse mask prediction, (2) spatiotemporal-aware token
+ *         permutation, (3) first-frame sink; TL;DR (3D window permutation,
+ *         blockwise representative tokens); Figure 2 and 3 captions.
+ *   [RF1] "RainFusion: Adaptive Video Generation Acceleration via
+ *         Multi-Dimensional Visual Redundancy" (arXiv 2505.21036): Abstract;
+ *         review page, Assumptions (softmax attention, Eq. (1)).
+ *
+ * One attention call of a diffusion transformer runs, on the caller's HIP
+ * stream:
+ *   rf_permute(Q), rf_permute(K), rf_permute(V, RF_TILES_T)   3D windows
+ *   rf_block_means(Qp, Kp)                                     Qbar, Kbar
+ *   rf_predict_mask(Qbar, Kbar)                                kept tiles
+ *   rf_sparse_attn(Qp, Kp, Vt, kept)                           Op
+ *   rf_unpermute(Op)                                           O
+ *
+ * Conventions
+ *   Token tensors are contiguous [B][H][tokens][d] (RF_ROWS).  Raster token
+ *   n = (t*H + h)*W + w of a T x H x W latent grid; n_text text tokens follow
+ *   the N = T*H*W video tokens.  The permuted sequence has Np padded video
+ *   slots (window order, pad slots zero) followed by the text tokens:
+ *   Lp = Np + n_text slots.  Blocks ("tiles") are bs = wt*wh*ww consecutive
+ *   slots: nb video blocks, then ceil(n_text/bs) text tiles.
+ *   Window order: blocks row-major over (frame, row, column) block
+ *   coordinates of the grid padded up to whole windows; tokens row-major
+ *   inside a block.  With permute = 0 the slots are the raster tokens and
+ *   the last block is padded.
+ *   All pointers passed to the GPU calls are device pointers that must be
+ *   16-byte aligned; calls only enqueue work on `stream` (never synchronise,
+ *   never allocate), and return before any launch when an argument is bad.
+ *   A plan is bound to the device that was current at rf_plan_create; call
+ *   the GPU functions with that device current.  Plans are immutable after
+ *   creation and may be shared by threads.
+ *   Errors: every function returns an rf_status; rf_last_error() gives a
+ *   thread-local message for the last failure.  Nothing aborts or prints.
+ */
+#ifndef RF_H
+#define RF_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RF_OK = 0,
+  RF_ERR_INVALID_ARG = 1,      /* null/misaligned pointer, bad size or value */
+  RF_ERR_UNSUPPORTED = 2,      /* valid but not implemented (d, bs, dtype) */
+  RF_ERR_HIP = 3,              /* HIP runtime error (no device, launch, copy) */
+  RF_ERR_BUFFER_TOO_SMALL = 4  /* host table buffer smaller than required */
+} rf_status;
+
+typedef enum { RF_F32 = 0, RF_BF16 = 1 } rf_dtype;
+
+/* Order of a permuted tensor in memory. */
+typedef enum {
+  RF_ROWS = 0,    /* [B][H][Lp][d]: one row of d values per slot */
+  RF_TILES_T = 1  /* [B][H][n_tiles][d][bs]: each tile transposed, the bs
+                     slots of one feature contiguous (pad slots zero).  The
+                     V operand of rf_sparse_attn uses this order. */
+} rf_order;
+
+/* Latent grid, window and switches of one attention call. */
+typedef struct {
+  int32_t T, H, W;      /* latent frames, rows, columns (T = 1 for images) */
+  int32_t wt, wh, ww;   /* window; bs = wt*wh*ww must be 64 or 128 */
+  int32_t n_text;       /* text tokens after the video tokens (>= 0) */
+  int32_t permute;      /* 1 = 3D window order [RF2 insight (2)], 0 = raster */
+  int32_t sink;         /* 1 = key blocks holding a frame-0 token are always
+                           kept [RF2 insight (3)] */
+} rf_layout;
+
+typedef struct {
+  int64_t N;            /* video tokens T*H*W */
+  int64_t Np;           /* padded video slots, nb*bs */
+  int64_t L;            /* N + n_text: rows of an unpermuted tensor */
+  int64_t Lp;           /* Np + n_text: rows of a permuted RF_ROWS tensor */
+  int32_t bs;           /* slots per block */
+  int32_t nb;           /* video blocks */
+  int32_t n_text_tiles; /* ceil(n_text / bs) */
+  int32_t n_tiles;      /* nb + n_text_tiles: query and key tiles */
+  int32_t n_sink;       /* sink blocks (0 when the sink is off) */
+} rf_sizes;
+
+/* Keep counts of the mask rule for one sparsity s (percent):
+ * k = floor((nb*(100 - s) + 50) / 100), k_eff = max(k, n_sink, 1).
+ * A video query tile keeps k_eff video blocks plus every text tile; a text
+ * query tile keeps all n_tiles tiles. */
+typedef struct {
+  int32_t k;
+  int32_t k_eff;
+  int32_t row_len_video;  /* k_eff + n_text_tiles */
+  int32_t row_len_text;   /* n_tiles */
+  int64_t nnz_per_head;   /* nb*row_len_video + n_text_tiles*row_len_text */
+} rf_keep;
+
+/* ---- host-only helpers (no device needed) ------------------------------ */
+
+/* Sizes of a layout.  RF_ERR_INVALID_ARG for non-positive grid or window
+ * extents, negative n_text, switches other than 0/1, or sizes beyond 2^31
+ * slots; RF_ERR_UNSUPPORTED when bs is not 64 or 128. */
+rf_status rf_layout_sizes(const rf_layout* lay, rf_sizes* out);
+
+/* The plan's index tables, into caller-owned host buffers of the given
+ * element capacities:
+ *   slot_src[Lp]   raster token of each slot, -1 for pad;
+ *   tok_slot[L]    slot of each raster token;
+ *   tile_count[n_tiles]  valid slots per tile;
+ *   is_sink[nb]    1 for sink blocks.
+ * RF_ERR_BUFFER_TOO_SMALL if a capacity is short. */
+rf_status rf_layout_tables(const rf_layout* lay, int32_t* slot_src,
+                           int64_t cap_slot_src, int32_t* tok_slot,
+                           int64_t cap_tok_slot, int32_t* tile_count,
+                           int64_t cap_tile_count, uint8_t* is_sink,
+                           int64_t cap_is_sink);
+
+/* Keep counts for sparsity_pct in [0, 99] [RF2 Abstract: 80% sparsity;
+ * Figure 2: 60% for image editing]. */
+rf_status rf_keep_count(const rf_layout* lay, int32_t sparsity_pct,
+                        rf_keep* out);
+
+const char* rf_status_str(rf_status s);
+const char* rf_last_error(void);
+
+/* ---- plan -------------------------------------------------------------- */
+
+typedef struct rf_plan rf_plan;   /* opaque: layout, sizes, device tables */
+
+/* Build the index tables of `lay` on the host and copy them to the current
+ * device (the only allocation and the only synchronising call of the
+ * library).  *out receives the plan, owned by the caller; RF_ERR_HIP when no
+ * device is usable. */
+rf_status rf_plan_create(const rf_layout* lay, rf_plan** out);
+void rf_plan_destroy(rf_plan* plan);
+rf_status rf_plan_sizes(const rf_plan* plan, rf_sizes* out);
+
+/* ---- hot path (asynchronous on `stream`) ------------------------------- */
+
+/* 3D window permutation [RF2 Abstract insight (2); TL;DR; Figure 3].
+ * x: [B][H][L][d] raster tokens (then text).  xp: permuted tensor in
+ * `order` (RF_ROWS: [B][H][Lp][d]; RF_TILES_T: [B][H][n_tiles][d][bs]).
+ * Pad slots are written as zeros.  dtype RF_BF16 or RF_F32; d in {64, 128}.
+ * x and xp must not overlap. */
+rf_status rf_permute(const rf_plan* plan, const void* x, void* xp, int32_t B,
+                     int32_t H, int32_t d, rf_dtype dtype, rf_order order,
+                     hipStream_t stream);
+
+/* Inverse permutation: xp [B][H][Lp][d] (RF_ROWS) -> x [B][H][L][d]; pad
+ * slots are dropped, text rows copied back. */
+rf_status rf_unpermute(const rf_plan* plan, const void* xp, void* x,
+                       int32_t B, int32_t H, int32_t d, rf_dtype dtype,
+                       hipStream_t stream);
+
+/* Representative tokens [RF2 Abstract insight (1)]: the mean of each video
+ * block's valid slots, accumulated in fp32.  qp, kp: [B][H][Lp][d]
+ * (RF_ROWS; pad slots are ignored whatever they hold).  qbar, kbar:
+ * fp32 [B][H][nb][d].  Text tiles are not pooled. */
+rf_status rf_block_means(const rf_plan* plan, const void* qp, const void* kp,
+                         float* qbar, float* kbar, int32_t B, int32_t H,
+                         int32_t d, rf_dtype dtype, hipStream_t stream);
+
+/* Online mask prediction [RF2 Abstract insights (1), (3)].  For each video
+ * query block i the logits l_ij = qbar_i . kbar_j / sqrt(d) (fp32) rank the
+ * non-sink video key blocks; the row keeps the sink blocks plus the
+ * k_eff - n_sink best blocks (ties to the lower index), then every text
+ * tile.  Text query tiles keep all tiles.
+ * kept_idx: int32 [B][H][nnz_per_head], rows in tile order, each row
+ * ascending (row r of a head starts at r*row_len_video for r < nb and at
+ * nb*row_len_video + (r - nb)*row_len_text after that).
+ * logits_or_null: optional fp32 [B][H][nb][nb] copy of l. */
+rf_status rf_predict_mask(const rf_plan* plan, const float* qbar,
+                          const float* kbar, int32_t B, int32_t H, int32_t d,
+                          int32_t sparsity_pct, int32_t* kept_idx,
+                          float* logits_or_null, hipStream_t stream);
+
+/* Block-sparse attention forward [RF2 Abstract: skipping computations for
+ * insignificant tokens; RF1 review, Eq. (1)].  For each valid query slot of
+ * tile i: o = sum_j softmax_j(scale * q . k_j) v_j over the valid slots of
+ * the tiles listed in row i of kept_idx; pad query rows are written as 0.
+ * qp, kp, op: [B][H][Lp][d] RF_ROWS; vt: [B][H][n_tiles][d][bs] RF_TILES_T.
+ * kept_idx as produced by rf_predict_mask for the same sparsity_pct; every
+ * entry must lie in [0, n_tiles).  RF_BF16: bf16 operands, fp32
+ * accumulation and softmax, bf16 output; RF_F32: fp32 throughout.
+ * d in {64, 128}. */
+rf_status rf_sparse_attn(const rf_plan* plan, const void* qp, const void* kp,
+                         const void* vt, const int32_t* kept_idx,
+                         int32_t sparsity_pct, void* op, int32_t B, int32_t H,
+                         int32_t d, float scale, rf_dtype dtype,
+                         hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RF_H */

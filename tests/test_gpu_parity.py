@@ -1,0 +1,257 @@
+"""Parity of the HIP path (through the C-ABI) with the fp64 oracle.
+
+Every case prints the case name before touching the GPU.  Shapes span several
+tiles with ragged windows, partial text tiles, raster blocks, both block
+sizes, both head dims and both precisions; the five synthetic workloads run
+at full size with all heads checked for the permutation, means and masks and
+sampled query tiles for attention (all tiles of two heads).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import parity
+from image_diffusion_dits_amd import configs, inputs, rf
+from oracle import rainfusion_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def run_gpu(plan, q, k, v, s, logits=False):
+    qp = rf.permute(plan, q)
+    kp = rf.permute(plan, k)
+    vt = rf.permute(plan, v, order=rf.TILES_T)
+    qbar, kbar = rf.block_means(plan, qp, kp)
+    kept, lg = rf.predict_mask(plan, qbar, kbar, s, logits=True)
+    op = rf.sparse_attn(plan, qp, kp, vt, kept, s)
+    o = rf.unpermute(plan, op)
+    torch.cuda.synchronize()
+    return dict(qp=qp, kp=kp, vt=vt, qbar=qbar, kbar=kbar, kept=kept,
+                logits=lg, op=op, o=o)
+
+
+def check_case(lay_dict, q, k, v, s, dtype, full_heads=None, sample_tiles=None,
+               seed=0, gpu=None):
+    """Run the GPU path on q, k, v (device tensors) and check it against the
+    oracle.  full_heads: heads whose every query tile is checked for
+    attention (None = all); other heads get `sample_tiles` random tiles."""
+    lay = parity.olayout(lay_dict)
+    z = orc.sizes(lay)
+    plan = rf.Plan(lay_dict)
+    g = gpu if gpu is not None else run_gpu(plan, q, k, v, s)
+    B, H = q.shape[:2]
+    qb, kb, vb = parity.bits(q), parity.bits(k), parity.bits(v)
+    qpb, kpb, vtb = parity.bits(g["qp"]), parity.bits(g["kp"]), parity.bits(g["vt"])
+    opb, ob = parity.bits(g["op"]), parity.bits(g["o"])
+    qbar, kbar = parity.values(g["qbar"]), parity.values(g["kbar"])
+    rows = rf.kept_rows(plan, g["kept"], s)
+    op = parity.values(g["op"])
+    valid = orc.slot_valid(lay)
+    rng = np.random.default_rng(seed)
+    stats = dict(swaps=0, max_abs=0.0, mean_abs=[])
+    for b in range(B):
+        for h in range(H):
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            # permutation, bit-exact
+            qpo = orc.permute(qb[sl], lay)
+            assert np.array_equal(qpb[sl], qpo), f"Q permutation b{b} h{h}"
+            kpo = orc.permute(kb[sl], lay)
+            assert np.array_equal(kpb[sl], kpo), f"K permutation b{b} h{h}"
+            vpo = orc.permute(vb[sl], lay)
+            assert np.array_equal(vtb[sl], parity.tiles_t(vpo, lay)), \
+                f"V permutation b{b} h{h}"
+            assert np.array_equal(ob[sl], orc.unpermute(opb[sl], lay)), \
+                f"unpermutation b{b} h{h}"
+            # means
+            qv = parity.values(g["qp"][b:b + 1, h:h + 1])
+            kv = parity.values(g["kp"][b:b + 1, h:h + 1])
+            qbo, kbo = orc.block_means(qv, lay), orc.block_means(kv, lay)
+            parity.check_means(qbar[sl], qbo)
+            parity.check_means(kbar[sl], kbo)
+            # mask
+            kept_o, l = orc.predict_mask(qbo, kbo, lay, s)
+            stats["swaps"] += parity.check_mask(rows[b][h], kept_o[0][0],
+                                                l[0, 0], lay, s)
+            # attention, with the GPU's kept rows
+            if full_heads is None or h in full_heads:
+                tiles = range(z["n_tiles"])
+            else:
+                tiles = sorted(rng.choice(z["n_tiles"], size=min(sample_tiles, z["n_tiles"]),
+                                          replace=False).tolist())
+            vv = parity.values(v[b:b + 1, h:h + 1])
+            want = orc.sparse_attention(qv, kv, orc.permute(vv, lay),
+                                        [[rows[b][h]]], lay,
+                                        query_tiles={(0, 0): tiles})
+            mx, mn = parity.check_attention(op[b, h], want[0, 0], valid, dtype)
+            stats["max_abs"] = max(stats["max_abs"], mx)
+            stats["mean_abs"].append(mn)
+    plan.close()
+    say(f"  swaps={stats['swaps']} max_abs={stats['max_abs']:.3e} "
+        f"mean_abs={np.mean(stats['mean_abs']):.3e}")
+    return g, stats
+
+
+def _iid(shape, seed, dtype):
+    return inputs.random_tensor(shape, seed, device="cuda", dtype=dtype)
+
+
+EDGE = [
+    # name, layout, B, H, d, dtype, sparsity
+    ("ragged3d-text77", dict(T=3, H=13, W=21, wt=2, wh=8, ww=8, n_text=77,
+                             permute=1, sink=1), 2, 3, 128, torch.bfloat16, 70),
+    ("bs64-d64", dict(T=2, H=10, W=9, wt=1, wh=8, ww=8, n_text=0, permute=1,
+                      sink=1), 1, 2, 64, torch.bfloat16, 50),
+    ("raster-bs64-text10", dict(T=3, H=7, W=11, wt=1, wh=8, ww=8, n_text=10,
+                                permute=0, sink=1), 1, 2, 128, torch.bfloat16, 60),
+    ("bs128-d64", dict(T=2, H=9, W=17, wt=2, wh=8, ww=8, n_text=0, permute=1,
+                       sink=0), 1, 2, 64, torch.bfloat16, 40),
+    ("f32-d128-bs128", dict(T=2, H=9, W=17, wt=2, wh=8, ww=8, n_text=5,
+                            permute=1, sink=1), 1, 2, 128, torch.float32, 40),
+    ("f32-d64-bs64-raster", dict(T=2, H=5, W=30, wt=1, wh=8, ww=8, n_text=64,
+                                 permute=0, sink=1), 1, 2, 64, torch.float32, 75),
+    ("single-block", dict(T=1, H=8, W=8, wt=1, wh=8, ww=8, n_text=0, permute=1,
+                          sink=0), 1, 1, 128, torch.bfloat16, 90),
+    ("dense-s0", dict(T=3, H=13, W=21, wt=2, wh=8, ww=8, n_text=77, permute=1,
+                      sink=1), 1, 2, 128, torch.bfloat16, 0),
+    ("max-s99", dict(T=3, H=13, W=21, wt=2, wh=8, ww=8, n_text=0, permute=1,
+                     sink=0), 1, 2, 128, torch.bfloat16, 99),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
+def test_edge_layouts(case):
+    name, lay, B, H, d, dt, s = case
+    say(f"[edge] {name} B={B} H={H} d={d} {dt} s={s}")
+    L = rf.layout_sizes(lay)["L"]
+    q = _iid((B, H, L, d), 11, dt)
+    k = _iid((B, H, L, d), 12, dt)
+    v = _iid((B, H, L, d), 13, dt)
+    check_case(lay, q, k, v, s, "bf16" if dt == torch.bfloat16 else "f32")
+
+
+def test_tiny_f32_workload():
+    cfg = configs.TINY
+    say(f"[workload] {cfg.name}")
+    q, k, v = (t.cuda() for t in inputs.make_qkv(cfg, "cpu"))
+    g, _ = check_case(cfg.layout, q, k, v, cfg.sparsity[0], "f32")
+    # the optional logits equal the oracle's block scores
+    lay = parity.olayout(cfg)
+    qbo = orc.block_means(parity.values(g["qp"]), lay)
+    kbo = orc.block_means(parity.values(g["kp"]), lay)
+    l, _ = orc.block_scores(qbo, kbo)
+    np.testing.assert_allclose(parity.values(g["logits"]), l, atol=1e-6)
+
+
+def test_image_bf16_workload():
+    cfg = configs.IMAGE
+    say(f"[workload] {cfg.name}")
+    q, k, v = (t.cuda() for t in inputs.make_qkv(cfg, "cpu"))
+    check_case(cfg.layout, q, k, v, cfg.sparsity[0], "bf16")
+
+
+def test_video720_workload():
+    cfg = configs.VIDEO720
+    say(f"[workload] {cfg.name} (all heads: permutation, means, mask; "
+        f"attention: heads 0 and {cfg.H // 2} in full, 16 tiles elsewhere)")
+    q, k, v = inputs.make_qkv(cfg, "cuda")
+    check_case(cfg.layout, q, k, v, cfg.sparsity[0], "bf16",
+               full_heads={0, cfg.H // 2}, sample_tiles=16)
+
+
+def test_video_long_text_workload():
+    cfg = configs.VIDEO_LONG
+    say(f"[workload] {cfg.name}")
+    q, k, v = inputs.make_qkv(cfg, "cuda")
+    check_case(cfg.layout, q, k, v, cfg.sparsity[0], "bf16",
+               full_heads={0, cfg.H // 2}, sample_tiles=16)
+
+
+@pytest.mark.parametrize("permute", [1, 0])
+def test_sweep_workload(permute):
+    cfg = configs.SWEEP if permute else configs.SWEEP_RASTER
+    q, k, v = inputs.make_qkv(cfg, "cuda", H=4)
+    for s in cfg.sparsity:
+        say(f"[workload] {cfg.name} s={s} (4 heads, 12 tiles each)")
+        check_case(cfg.layout, q, k, v, s, "bf16", full_heads=set(),
+                   sample_tiles=12, seed=s)
+
+
+def test_repeated_runs_are_bitwise_identical():
+    cfg = configs.VIDEO720
+    say("[determinism] three runs of the 720p case (8 heads)")
+    q, k, v = inputs.make_qkv(cfg, "cuda", H=8)
+    plan = rf.Plan(cfg.layout)
+    outs = [run_gpu(plan, q, k, v, 80) for _ in range(3)]
+    for key in ("qp", "kp", "vt", "qbar", "kbar", "kept", "op", "o"):
+        a = parity.bits(outs[0][key]) if outs[0][key].dtype != torch.int32 \
+            else outs[0][key].cpu().numpy()
+        for other in outs[1:]:
+            b = parity.bits(other[key]) if other[key].dtype != torch.int32 \
+                else other[key].cpu().numpy()
+            assert np.array_equal(a, b), key
+    # The sweep's 80% point is the 720p case itself.
+    sw = configs.SWEEP
+    q2, k2, v2 = inputs.make_qkv(sw, "cuda", H=8)
+    assert torch.equal(q, q2) and torch.equal(k, k2) and torch.equal(v, v2)
+    plan.close()
+
+
+def test_out_of_range_kept_entries_are_skipped():
+    """Tile ids outside [0, n_tiles) are ignored by the kernel's own bounds
+    check: rows [0, -7, 2, 3] give the attention over tiles 0, 2 and 3."""
+    lay = dict(T=2, H=8, W=16, wt=1, wh=8, ww=8, n_text=0, permute=1, sink=0)
+    say("[robustness] kept lists with out-of-range ids")
+    plan = rf.Plan(lay)
+    z = plan.sizes
+    olay = parity.olayout(lay)
+    for dt in (torch.bfloat16, torch.float32):
+        q, k, v = (_iid((1, 1, z["L"], 128), s, dt) for s in (1, 2, 3))
+        qp, kp = rf.permute(plan, q), rf.permute(plan, k)
+        vt = rf.permute(plan, v, order=rf.TILES_T)
+        kept = torch.tensor([[[0, 1, 2, 3]]], dtype=torch.int32)
+        kept = kept.repeat(1, 1, z["nb"]).cuda()      # s = 0: rows of nb = 4
+        ref = rf.sparse_attn(plan, qp, kp, vt, kept, 0)
+        bad = kept.clone()
+        bad[0, 0, 1::4] = -7
+        bad[0, 0, 5] = 1 << 30                          # row 1: huge id too
+        bad[0, 0, 4] = 0
+        got = rf.sparse_attn(plan, qp, kp, vt, bad, 0)
+        torch.cuda.synchronize()
+        rows = [[[np.array([0, 2, 3])] * z["n_tiles"]]]
+        want = orc.sparse_attention(parity.values(qp), parity.values(kp),
+                                    orc.permute(parity.values(v), olay), rows, olay)
+        parity.check_attention(parity.values(got)[0, 0], want[0, 0],
+                               orc.slot_valid(olay),
+                               "bf16" if dt == torch.bfloat16 else "f32")
+        assert not torch.equal(ref, got)
+    plan.close()
+
+
+def test_gpu_argument_errors():
+    plan = rf.Plan(configs.TINY.layout)
+    z = plan.sizes
+    x = torch.zeros(1, 2, z["L"], 64, device="cuda")
+    with pytest.raises(rf.RfError) as e:
+        rf.permute(plan, x[..., :48].contiguous())       # d = 48
+    assert e.value.status == rf.ERR_UNSUPPORTED
+    L = rf.lib()
+    xp = torch.zeros(1, 2, z["Lp"], 64, device="cuda")
+    mis = x.view(-1)[1:].data_ptr()                     # 4-byte aligned only
+    st = L.rf_permute(plan.handle, mis, xp.data_ptr(), 1, 2, 64, rf.F32,
+                      rf.ROWS, None)
+    assert st == rf.ERR_INVALID_ARG
+    kept = torch.zeros(10, dtype=torch.int32, device="cuda")
+    st = L.rf_sparse_attn(plan.handle, xp.data_ptr(), xp.data_ptr(), xp.data_ptr(),
+                          kept.data_ptr(), 50, xp.data_ptr(), 1, 2, 64, -1.0,
+                          rf.F32, None)
+    assert st == rf.ERR_INVALID_ARG
+    st = L.rf_predict_mask(plan.handle, xp.data_ptr(), xp.data_ptr(), 1, 2, 64, 100,
+                           kept.data_ptr(), None, None)
+    assert st == rf.ERR_INVALID_ARG
+    plan.close()
