@@ -126,10 +126,11 @@ __global__ __launch_bounds__(kThreads) void predict_mask_kernel(
       if (eq && eq_seen + popc64(eqm & lt_mask) < n_eq_take) keep = true;
       eq_seen += popc64(eqm);
       const uint64_t km = __ballot(keep);
-      if (keep) out[pos + popc64(km & lt_mask)] = j;
+      const int at = pos + popc64(km & lt_mask);
+      if (keep && at < k_eff) out[at] = j;
       pos += popc64(km);
     }
-    for (int t = lane; t < n_tt; t += 64) out[pos + t] = nb + t;
+    for (int t = lane; t < n_tt; t += 64) out[k_eff + t] = nb + t;
   }
 }
 
@@ -149,6 +150,9 @@ void launch(const rf_plan* p, const float* qbar, const float* kbar,
             hipStream_t st) {
   const int nb = p->sz.nb;
   const size_t lds = sizeof(float) * (size_t(R) * D + size_t(R) * nb);
+  (void)hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&predict_mask_kernel<D, R>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   dim3 grid((nb + R - 1) / R, BH);
   hipLaunchKernelGGL((predict_mask_kernel<D, R>), grid, dim3(kThreads), lds, st,
                      qbar, kbar, p->is_sink, kept, logits, nb, p->sz.n_sink,
