@@ -1,0 +1,277 @@
+"""Benchmark of the RainFusion2.0 sparse-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
+                    [--sparsity S] [--raster] [--no-cpu-baseline]
+
+One step is one pass of the whole path over one attention call of the
+workload: permute Q, K, V (3D windows), pool block means, predict the mask,
+block-sparse attention, unpermute O.  Inputs are synthetic (seeded) and
+resident in HBM before timing starts; every output buffer is allocated
+beforehand, so the timed region only launches kernels.
+
+Prints one JSON line.  `value` is executed attention TFLOP/s over the whole
+step: 4*d*bs^2 FLOP per kept (query tile, key tile) pair, summed over heads,
+divided by the step time.  `roofline` reports the attention kernel alone
+against the bf16 dense MFMA peak (its duration from HIP events on the
+stream it runs on), and `cpu_baseline` times the fp64 oracle on a bounded
+sample of the same workload on the host's cores.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "block-sparse attn TFLOP/s, ms/call @75.6k tok 80% sparse, MFMA util"
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+ATTN_SRC = os.path.join(ROOT, "image_diffusion_dits_amd", "csrc", "attn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--sparsity", type=int, default=None)
+    ap.add_argument("--raster", action="store_true",
+                    help="permutation off (raster blocks)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tiles", type=int, default=660,
+                    help="query tiles in the oracle's attention sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after timing, run a plain elementwise copy of "
+                         "known size (counter calibration)")
+    return ap.parse_args()
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def stored_traffic(workload, per_launch_flop):
+    """HBM bytes per attention launch from committed rocprofv3 counter runs,
+    or None when absent or taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("attn_src_sha256") != source_hash(ATTN_SRC):
+        return None
+    if rec.get("workload") != workload:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, q, k, v, sparsity, n_tiles_sample, exec_flop_total):
+    """Time the fp64 oracle on one head: the whole of permute, means, mask
+    and unpermute, plus attention on a sample of query tiles; extrapolate to
+    all heads and tiles (heads are independent and every video row keeps the
+    same number of tiles)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import rainfusion_oracle as orc
+
+    lay = orc.Layout(**{key: cfg.layout[key] for key in
+                        ("T", "H", "W", "wt", "wh", "ww", "n_text", "permute", "sink")})
+    z = orc.sizes(lay)
+    f64 = lambda t: t[:1, :1].cpu().double().numpy()
+    qh, kh, vh = f64(q), f64(k), f64(v)
+    t0 = time.perf_counter()
+    qp, kp, vp = (orc.permute(x, lay) for x in (qh, kh, vh))
+    qbar, kbar = orc.block_means(qp, lay), orc.block_means(kp, lay)
+    kept, _ = orc.predict_mask(qbar, kbar, lay, sparsity)
+    t1 = time.perf_counter()
+    rng = np.random.default_rng(0)
+    tiles = sorted(rng.choice(z["nb"], size=min(n_tiles_sample, z["nb"]),
+                              replace=False).tolist())
+    op = orc.sparse_attention(qp, kp, vp, kept, lay, query_tiles={(0, 0): tiles})
+    t2 = time.perf_counter()
+    op[np.isnan(op)] = 0.0
+    orc.unpermute(op, lay)
+    t3 = time.perf_counter()
+    per_head_fixed = (t1 - t0) + (t3 - t2)
+    per_tile = (t2 - t1) / len(tiles)
+    H = cfg.H * cfg.B
+    full = H * per_head_fixed + H * z["n_tiles"] * per_tile
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {
+        "value": exec_flop_total / full / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"head 0 of {H}: permute, means, mask, unpermute in full; "
+                   f"attention on {len(tiles)} of {z['n_tiles']} query tiles; "
+                   f"{t3 - t0:.1f} s measured, extrapolated to all heads "
+                   f"and tiles ({full:.0f} s per step)"),
+    }
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported "
+              "(every step is independent per head; the multi-GPU layout is "
+              "head sharding, not run here)", file=sys.stderr)
+        return 2
+    import torch
+
+    from image_diffusion_dits_amd import configs, inputs, rf
+
+    cfg = configs.get(a.config)
+    if a.raster:
+        cfg = configs.SWEEP_RASTER if a.config in (3, 5) else cfg
+    s = a.sparsity if a.sparsity is not None else (80 if a.config == 5 else cfg.sparsity[0])
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    q, k, v = inputs.make_qkv(cfg, dev)
+    plan = rf.Plan(cfg.layout)
+    z = plan.sizes
+    kc = plan.keep(s)
+    B, H, d = cfg.B, cfg.H, cfg.d
+    bs = z["bs"]
+
+    # Every buffer is allocated before timing.
+    qp = torch.empty(B, H, z["Lp"], d, dtype=q.dtype, device=dev)
+    kp = torch.empty_like(qp)
+    vt = torch.empty(B, H, z["n_tiles"], d, bs, dtype=q.dtype, device=dev)
+    qbar = torch.empty(B, H, z["nb"], d, dtype=torch.float32, device=dev)
+    kbar = torch.empty_like(qbar)
+    kept = torch.empty(B, H, kc["nnz_per_head"], dtype=torch.int32, device=dev)
+    op = torch.empty_like(qp)
+    o = torch.empty_like(q)
+
+    stages = ["permute_qkv", "block_means", "predict_mask", "sparse_attn", "unpermute"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        rf.permute(plan, q, out=qp)
+        rf.permute(plan, k, out=kp)
+        rf.permute(plan, v, order=rf.TILES_T, out=vt)
+        mark(1)
+        rf.block_means(plan, qp, kp, qbar, kbar)
+        mark(2)
+        rf.predict_mask(plan, qbar, kbar, s, kept=kept)
+        mark(3)
+        rf.sparse_attn(plan, qp, kp, vt, kept, s, out=op)
+        mark(4)
+        rf.unpermute(plan, op, out=o)
+        mark(5)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region 1: whole steps, wall clock.
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / a.steps
+
+    # Timed region 2: the same steps with HIP events between stages (all
+    # kernels run on torch's current stream, which the events are recorded on).
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)]
+           for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    for i in range(a.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    stage_ms = {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / a.steps
+                for j, name in enumerate(stages)}
+    ev_step_ms = sum(e[0].elapsed_time(e[5]) for e in evs) / a.steps
+
+    pairs = kc["nnz_per_head"] * B * H
+    exec_flop = 4.0 * d * bs * bs * pairs
+    L = z["L"]
+    dense_flop = 4.0 * B * H * L * L * d
+    attn_s = stage_ms["sparse_attn"] / 1e3
+    ms_step = wall * 1e3
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    attn_tflops = exec_flop / attn_s / 1e12
+    workload = cfg.name + ("" if cfg.permute else "-raster")
+    traffic = stored_traffic(workload, exec_flop)
+    aux_ms = sum(stage_ms[n] for n in stages if n != "sparse_attn")
+    esize = 2 if cfg.dtype == "bf16" else 4
+    perm_bytes = 3 * B * H * (z["L"] + z["Lp"]) * d * esize
+    unperm_bytes = B * H * 2 * z["L"] * d * esize
+    pool_bytes = 2 * B * H * z["Np"] * d * esize
+
+    rec = {
+        "metric": METRIC,
+        "value": round(exec_flop / wall / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": workload, "batch": B, "heads": H, "head_dim": d,
+            "tokens": z["N"], "text_tokens": z["L"] - z["N"],
+            "padded_slots": z["Lp"], "block": bs, "blocks": z["nb"],
+            "sparsity_pct": s, "kept_tiles_per_row": kc["k_eff"],
+            "kept_tile_pairs": pairs, "sink_blocks": z["n_sink"],
+        },
+        "attn_ms": round(stage_ms["sparse_attn"], 4),
+        "attn_exec_tflops": round(attn_tflops, 2),
+        "attn_dense_equiv_tflops": round(dense_flop / attn_s / 1e12, 2),
+        "mfma_util": round(attn_tflops / peak, 4),
+        "exec_tflop_per_call": round(exec_flop / 1e12, 4),
+        "dense_equiv_tflop_per_call": round(dense_flop / 1e12, 4),
+        "stages_ms": {n: round(x, 4) for n, x in stage_ms.items()},
+        "event_ms_per_step": round(ev_step_ms, 4),
+        "mask_plus_perm_over_attn": round(aux_ms / stage_ms["sparse_attn"], 4),
+        "hbm_gbs": {
+            "permute_qkv": round(perm_bytes / (stage_ms["permute_qkv"] / 1e3) / 1e9, 1),
+            "block_means": round(pool_bytes / (stage_ms["block_means"] / 1e3) / 1e9, 1),
+            "unpermute": round(unperm_bytes / (stage_ms["unpermute"] / 1e3) / 1e9, 1),
+        },
+        "roofline": {
+            "kernel": "attn_bf16_kernel" if cfg.dtype == "bf16" else "attn_f32_kernel",
+            "bound": "mfma",
+            "achieved": round(attn_tflops, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / peak, 4),
+            "traffic": traffic,
+        },
+    }
+    if a.copy_probe:
+        # torch.neg reads and writes exactly n*2 bytes: a plain copy kernel
+        # whose HBM counters calibrate the attention kernel's.
+        n = 1 << 29
+        src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        rec["copy_probe_bytes"] = {"read": 2 * n, "write": 2 * n}
+    if not a.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(cfg, q, k, v, s, a.cpu_tiles, exec_flop)
+    print(json.dumps(rec), flush=True)
+    plan.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -64,18 +64,39 @@ __device__ inline int64_t row_offset(int32_t tile, int32_t nb,
 
 // ---------------------------------------------------------------- bf16 MFMA
 
+typedef __attribute__((address_space(3))) void lds_void;
+
 template <int D, int BS>
 struct Bf16Cfg {
   static constexpr int kWaves = BS / 32;
   static constexpr int kThreads = kWaves * 64;
-  static constexpr int kKStride = D + 8;    // K row in LDS (bf16)
-  static constexpr int kVStride = BS + 4;   // V^T row in LDS (bf16)
-  static constexpr int kKChunks = BS * D / 8;  // 16-byte chunks per tile
-  static constexpr int kPerThread = kKChunks / kThreads;
+  static constexpr int kKRowBytes = D * 2;     // one K row (bf16)
+  static constexpr int kVRowBytes = BS * 2;    // one V^T row (bf16)
+  static constexpr int kKChunks = BS * D / 8;  // 16-byte chunks per K tile
+  static constexpr int kVChunks = D * BS / 8;  // 16-byte chunks per V^T tile
+  static constexpr int kKLoads = kKChunks / kThreads;  // per thread
+  static constexpr int kVLoads = kVChunks / kThreads;
+  static_assert(kKChunks % kThreads == 0 && kVChunks % kThreads == 0, "tile");
 };
 
+// XOR swizzle of the 16-byte chunks of an LDS row.  Rows of 256 bytes span
+// all 64 banks, so chunk p of row r is stored at p ^ (r % 16); rows of 128
+// bytes pair up per bank sweep, so at p ^ ((r / 2) % 8).  Either way the 16
+// lanes of one ds_read_b128 phase, which read one chunk column of 16
+// consecutive rows, land on 16 distinct bank groups.
+template <int ROW_BYTES>
+__device__ inline int swz(int row) {
+  if constexpr (ROW_BYTES >= 256) return row % 16;
+  else return (row / 2) % 8;
+}
+
+// sigma swaps bits 2 and 3 of a row index inside a 32-row MFMA block.
+__device__ inline int sigma(int x) {
+  return (x & ~0xC) | ((x & 4) << 1) | ((x & 8) >> 1);
+}
+
 template <int D, int BS>
-__global__ __launch_bounds__((BS / 32) * 64) void attn_bf16_kernel(
+__global__ __launch_bounds__((BS / 32) * 64, 2) void attn_bf16_kernel(
     const __bf16* __restrict__ qp, const __bf16* __restrict__ kp,
     const __bf16* __restrict__ vt, const int32_t* __restrict__ kept,
     __bf16* __restrict__ op, const uint32_t* __restrict__ tile_bits,
@@ -83,8 +104,8 @@ __global__ __launch_bounds__((BS / 32) * 64) void attn_bf16_kernel(
     int32_t nb, int32_t n_tt, int32_t row_len_video, int64_t nnz,
     float scale_log2) {
   using C = Bf16Cfg<D, BS>;
-  __shared__ __align__(16) __bf16 ks[BS * C::kKStride];
-  __shared__ __align__(16) __bf16 vs[D * C::kVStride];
+  __shared__ __align__(16) __bf16 ks[BS * D];   // K tile, swizzled rows
+  __shared__ __align__(16) __bf16 vs[D * BS];   // V^T tile, swizzled rows
   const int32_t n_tiles = nb + n_tt;
   const TileJob job = job_of(blockIdx.x, BH, nb, n_tt);
   const int64_t bh = job.bh;
@@ -114,112 +135,148 @@ __global__ __launch_bounds__((BS / 32) * 64) void attn_bf16_kernel(
   for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  uint4 pk[C::kPerThread], pv[C::kPerThread];
-  auto fetch = [&](int32_t kt) {
+  // Global -> LDS copies of one K and one V^T tile (global_load_lds_dwordx4:
+  // lane l of a wave instruction lands at LDS base + 16 l, so the LDS
+  // position is fixed and the swizzle is applied to the source chunk).
+  auto load_tile = [&](int32_t kt) {
+    const int64_t last = Lp - 1;
 #pragma unroll
-    for (int u = 0; u < C::kPerThread; ++u) {
-      const int c = threadIdx.x + u * C::kThreads;
-      const int r = c / (D / 8), cc = c % (D / 8);
-      const int64_t slot = int64_t(kt) * BS + r;
-      pk[u] = slot < Lp ? *reinterpret_cast<const uint4*>(kh + slot * D + cc * 8)
-                        : make_uint4(0, 0, 0, 0);
-      const int vr = c / (BS / 8), vc = c % (BS / 8);
-      pv[u] = *reinterpret_cast<const uint4*>(vh + (int64_t(kt) * D + vr) * BS + vc * 8);
+    for (int u = 0; u < C::kKLoads; ++u) {
+      const int base = (u * C::kWaves + wave) * 64;   // first chunk of this instruction
+      const int pch = base + lane;
+      constexpr int CPR = C::kKRowBytes / 16;
+      const int r = pch / CPR, pc = pch % CPR;
+      const int gc = pc ^ swz<C::kKRowBytes>(r);
+      int64_t slot = int64_t(kt) * BS + r;
+      slot = slot < last ? slot : last;               // pad rows of a last text tile
+      __builtin_amdgcn_global_load_lds(
+          static_cast<const void*>(kh + slot * D + gc * 8),
+          (lds_void*)(ks + base * 8), 16, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < C::kVLoads; ++u) {
+      const int base = (u * C::kWaves + wave) * 64;
+      const int pch = base + lane;
+      constexpr int CPR = C::kVRowBytes / 16;
+      const int r = pch / CPR, pc = pch % CPR;
+      const int gc = pc ^ swz<C::kVRowBytes>(r);
+      __builtin_amdgcn_global_load_lds(
+          static_cast<const void*>(vh + (int64_t(kt) * D + r) * BS + gc * 8),
+          (lds_void*)(vs + base * 8), 16, 0, 0);
     }
   };
-  auto stash = [&]() {
-#pragma unroll
-    for (int u = 0; u < C::kPerThread; ++u) {
-      const int c = threadIdx.x + u * C::kThreads;
-      const int r = c / (D / 8), cc = c % (D / 8);
-      *reinterpret_cast<uint4*>(ks + r * C::kKStride + cc * 8) = pk[u];
-      const int vr = c / (BS / 8), vc = c % (BS / 8);
-      uint2* vd = reinterpret_cast<uint2*>(vs + vr * C::kVStride + vc * 8);
-      vd[0] = make_uint2(pv[u].x, pv[u].y);
-      vd[1] = make_uint2(pv[u].z, pv[u].w);
-    }
-  };
-  auto valid_tile = [&](int32_t kt) { return kt >= 0 && kt < n_tiles; };
 
-  int it = 0;
-  while (it < row_len && !valid_tile(row[it])) ++it;
-  if (it < row_len) fetch(row[it]);
-  while (it < row_len) {
+  // LDS element offsets of this lane's operand chunks.
+  //   K (A of S^T): row kb*32 + sigma(li), chunk 2m + g.
+  //   V^T (A of O^T): row db*32 + li, chunk 4kb + 2h + g.
+  const int krow0 = sigma(li);
+  const int kswz = swz<C::kKRowBytes>(krow0);  // kb*32 does not change it
+  const int vswz = swz<C::kVRowBytes>(li);     // nor does db*32
+
+  for (int it = 0; it < row_len; ++it) {
     const int32_t kt = row[it];
-    int nxt = it + 1;
-    while (nxt < row_len && !valid_tile(row[nxt])) ++nxt;
-    __syncthreads();
-    stash();
-    __syncthreads();
-    if (nxt < row_len) fetch(row[nxt]);
+    if (kt < 0 || kt >= n_tiles) continue;            // uniform across the WG
+    __syncthreads();                                  // previous tile consumed
+    load_tile(kt);
+    __syncthreads();                                  // waits for the copies
 
-    // S^T blocks: s[kb] covers keys kb*32 .. +32 (rows) x the wave's 32
-    // queries (columns).  Lane (li, g), element r: key 8(r/4) + 4g + r%4.
-    f32x16 s[BS / 32];
-#pragma unroll
-    for (int kb = 0; kb < BS / 32; ++kb) {
-      s[kb] = f32x16{};
-      const __bf16* ka = ks + (kb * 32 + li) * C::kKStride + 8 * g;
-#pragma unroll
-      for (int m = 0; m < D / 16; ++m)
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            *reinterpret_cast<const bf16x8*>(ka + 16 * m), qf[m], s[kb], 0, 0, 0);
-    }
+    // The tile is processed in key groups of KG*32 keys (online softmax per
+    // group), which bounds the live S and P registers.
+    constexpr int KG = 1;
     const bool full = tile_count[kt] == BS;
-    float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < BS / 32; ++kb) {
-      const uint32_t bits = full ? 0xffffffffu : tile_bits[kt * 4 + kb];
+    for (int grp = 0; grp < BS / 32 / KG; ++grp) {
+      // S^T blocks: s[j] covers keys (grp*KG + j)*32 .. +32 (rows) x the
+      // wave's 32 queries (columns).  MFMA row x of block kb is fed K row
+      // kb*32 + sigma(x), so accumulator register r = 4a + b of lane group g
+      // holds key
+      //   kb*32 + 16(a/2) + 8g + 4(a%2) + b,
+      // which makes the 8 keys behind registers 8h .. 8h+7 contiguous
+      // (kb*32 + 16h + 8g .. +8): the P V product then reads V^T with one
+      // 16-byte LDS access per operand.
+      f32x16 s[KG];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 8 * (r / 4) + 4 * g + (r % 4);
-        float x = s[kb][r] * scale_log2;
-        if (!((bits >> key) & 1u)) x = -INFINITY;
-        s[kb][r] = x;
-        mx = fmaxf(mx, x);
+      for (int j = 0; j < KG; ++j) {
+        const int kb = grp * KG + j;
+        s[j] = f32x16{};
+        const __bf16* ka = ks + (kb * 32 + krow0) * D;
+#pragma unroll
+        for (int m = 0; m < D / 16; ++m)
+          s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              *reinterpret_cast<const bf16x8*>(ka + ((2 * m + g) ^ kswz) * 8), qf[m],
+              s[j], 0, 0, 0);
       }
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    float psum = 0.f;
-    bf16x8 pb[BS / 32][2];
+      // Row max over the group (raw dot products; the scale is positive).
+      float mx = -INFINITY;
+      if (full) {
 #pragma unroll
-    for (int kb = 0; kb < BS / 32; ++kb) {
+        for (int j = 0; j < KG; ++j)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        f32x8 p;
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[j][r]);
+      } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = __builtin_amdgcn_exp2f(s[kb][8 * h + e] - m_new);
-          psum += p[e];
+        for (int j = 0; j < KG; ++j) {
+          const uint32_t bits = tile_bits[kt * 4 + grp * KG + j];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int a = r / 4, b = r % 4;
+            const int key = 16 * (a / 2) + 8 * g + 4 * (a % 2) + b;
+            const float x = ((bits >> key) & 1u) ? s[j][r] : -INFINITY;
+            s[j][r] = x;
+            mx = fmaxf(mx, x);
+          }
         }
-        pb[kb][h] = __builtin_convertvector(p, bf16x8);
       }
-    }
-    l_run = l_run * alpha + psum;
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      // Lazy rescaling: the running max only moves (and O, l are
+      // rescaled) when some query's group max exceeds it by more than 8 in
+      // log2 units; otherwise exponents stay below 2^8 relative to the
+      // stale max, which fp32 accumulation and bf16 P absorb.  The final
+      // 1/l uses the same reference, so the result is unchanged.  A group
+      // whose keys are all pad for this query gives mx = -inf and no move.
+      const float mt = mx * scale_log2;
+      if (__ballot(mt > m_run + 8.f) != 0) {
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
-
-    // O^T[db] += V^T[db rows, keys] P^T.  For MFMA (kb, h) the k slots of
-    // lane group g, element e are keys kb*32 + 16h + 8(e/4) + 4g + e%4,
-    // matching the S^T accumulator registers 8h .. 8h+7.
+        for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+      }
+      const float neg_m = -m_run;
+      float psum = 0.f;
+      bf16x8 pb[KG][2];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const __bf16* va = vs + (db * 32 + li) * C::kVStride + 4 * g;
-#pragma unroll
-      for (int kb = 0; kb < BS / 32; ++kb) {
+      for (int j = 0; j < KG; ++j) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(va + kb * 32 + 16 * h);
-          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(va + kb * 32 + 16 * h + 8);
-          const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][h], o[db], 0, 0, 0);
+          f32x8 p;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            p[e] = __builtin_amdgcn_exp2f(fmaf(s[j][8 * h + e], scale_log2, neg_m));
+            psum += p[e];
+          }
+          pb[j][h] = __builtin_convertvector(p, bf16x8);
+        }
+      }
+      l_run += psum;
+
+      // O^T[db] += V^T[db rows, keys] P^T.  MFMA (kb, h): the k slots of
+      // lane group g are keys kb*32 + 16h + 8g .. +8 (see sigma above).
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const __bf16* va = vs + (db * 32 + li) * BS;
+#pragma unroll
+        for (int j = 0; j < KG; ++j) {
+          const int kb = grp * KG + j;
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                *reinterpret_cast<const bf16x8*>(va + ((4 * kb + 2 * h + g) ^ vswz) * 8),
+                pb[j][h], o[db], 0, 0, 0);
         }
       }
     }
-    it = nxt;
   }
 
   // Lane (li, g) holds O^T[dd = db*32 + 8a + 4g + b][query li].
@@ -229,14 +286,13 @@ __global__ __launch_bounds__((BS / 32) * 64) void attn_bf16_kernel(
   const bool qvalid = (tile_bits[qtile * 4 + qs / 32] >> (qs % 32)) & 1u;
   const float inv = (qvalid && l_tot > 0.f) ? 1.f / l_tot : 0.f;
   __bf16* dst = op + (bh * Lp + qrow) * D + 4 * g;
+  typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      float4 v4 = make_float4(o[db][4 * a] * inv, o[db][4 * a + 1] * inv,
-                              o[db][4 * a + 2] * inv, o[db][4 * a + 3] * inv);
-      typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
-      const f32x4 f = {v4.x, v4.y, v4.z, v4.w};
+      const f32x4 f = {o[db][4 * a] * inv, o[db][4 * a + 1] * inv,
+                       o[db][4 * a + 2] * inv, o[db][4 * a + 3] * inv};
       *reinterpret_cast<bf16x4*>(dst + db * 32 + 8 * a) = __builtin_convertvector(f, bf16x4);
     }
   }
