@@ -143,7 +143,7 @@ def main():
     bs = z["bs"]
 
     # Every buffer is allocated before timing.
-    qp = torch.empty(B, H, z["Lp"], d, dtype=q.dtype, device=dev)
+    qp = torch.empty(B, H, z["Lt"], d, dtype=q.dtype, device=dev)
     kp = torch.empty_like(qp)
     vt = torch.empty(B, H, z["n_tiles"], d, bs, dtype=q.dtype, device=dev)
     qbar = torch.empty(B, H, z["nb"], d, dtype=torch.float32, device=dev)
@@ -208,7 +208,7 @@ def main():
     traffic = stored_traffic(workload, exec_flop)
     aux_ms = sum(stage_ms[n] for n in stages if n != "sparse_attn")
     esize = 2 if cfg.dtype == "bf16" else 4
-    perm_bytes = 3 * B * H * (z["L"] + z["Lp"]) * d * esize
+    perm_bytes = 3 * B * H * (z["L"] + z["Lt"]) * d * esize
     unperm_bytes = B * H * 2 * z["L"] * d * esize
     pool_bytes = 2 * B * H * z["Np"] * d * esize
 

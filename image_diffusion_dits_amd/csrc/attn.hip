@@ -65,6 +65,7 @@ __device__ inline int64_t row_offset(int32_t tile, int32_t nb,
 // ---------------------------------------------------------------- bf16 MFMA
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void global_cvoid;
 
 template <int D, int BS>
 struct Bf16Cfg {
@@ -95,39 +96,64 @@ __device__ inline int sigma(int x) {
   return (x & ~0xC) | ((x & 4) << 1) | ((x & 8) >> 1);
 }
 
+// Lane offset (bytes) of a wave's global -> LDS copies of one tile whose
+// LDS rows are ROW_BYTES long: copy u of wave w moves 16-byte chunk
+// u*THREADS + w*64 + lane of the tile.  When the rows advanced per copy are
+// a multiple of 16 the swizzle of the copied row, and so the offset, is the
+// same for every copy; otherwise it alternates between two values.
+template <int ROW_BYTES, int THREADS>
+struct CopyPlan {
+  static constexpr int kCpr = ROW_BYTES / 16;          // chunks per row
+  static constexpr int kRowsPerCopy = THREADS / kCpr;  // rows per copy step
+  static constexpr int kVariants = (kRowsPerCopy % 16 == 0) ? 1 : 2;
+  // Global byte offset, inside the tile, of the chunk this lane copies in
+  // copy u (u < kVariants gives the per-lane part; add u*kRowsPerCopy rows).
+  __device__ static uint32_t lane_offset(int wave, int lane, int u) {
+    const int pch = u * THREADS + wave * 64 + lane;
+    const int r = pch / kCpr, pc = pch % kCpr;
+    const int gc = pc ^ swz<ROW_BYTES>(r);
+    return uint32_t(((r - u * kRowsPerCopy) * ROW_BYTES) + gc * 16);
+  }
+};
+
 template <int D, int BS>
 __global__ __launch_bounds__((BS / 32) * 64, 2) void attn_bf16_kernel(
     const __bf16* __restrict__ qp, const __bf16* __restrict__ kp,
     const __bf16* __restrict__ vt, const int32_t* __restrict__ kept,
     __bf16* __restrict__ op, const uint32_t* __restrict__ tile_bits,
-    const int32_t* __restrict__ tile_count, int64_t Lp, int32_t BH,
+    const int32_t* __restrict__ tile_count, int64_t Lt, int32_t BH,
     int32_t nb, int32_t n_tt, int32_t row_len_video, int64_t nnz,
     float scale_log2) {
   using C = Bf16Cfg<D, BS>;
+  using KCopy = CopyPlan<C::kKRowBytes, C::kThreads>;
+  using VCopy = CopyPlan<C::kVRowBytes, C::kThreads>;
   __shared__ __align__(16) __bf16 ks[BS * D];   // K tile, swizzled rows
   __shared__ __align__(16) __bf16 vs[D * BS];   // V^T tile, swizzled rows
   const int32_t n_tiles = nb + n_tt;
   const TileJob job = job_of(blockIdx.x, BH, nb, n_tt);
   const int64_t bh = job.bh;
   const int32_t qtile = job.tile;
-  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  const int lane = threadIdx.x % 64;
   const int li = lane % 32, g = lane / 32;
 
-  const __bf16* kh = kp + bh * Lp * D;
-  const __bf16* vh = vt + bh * int64_t(n_tiles) * D * BS;
-  const int32_t* row = kept + bh * nnz + row_offset(qtile, nb, row_len_video, n_tiles);
+  const char* kh = reinterpret_cast<const char*>(kp + bh * Lt * D);
+  const char* vh = reinterpret_cast<const char*>(vt + bh * int64_t(n_tiles) * D * BS);
+  // The kept row is read through the constant address space: uniform
+  // scalar loads that do not wait on the tile copies in flight.
+  const __attribute__((address_space(4))) int32_t* row =
+      (const __attribute__((address_space(4))) int32_t*)(
+          kept + bh * nnz + row_offset(qtile, nb, row_len_video, n_tiles));
   const int32_t row_len = qtile < nb ? row_len_video : n_tiles;
 
   // Q operand (B of S^T = K Q^T): lane (li, g) holds q[li][16m + 8g .. +8].
   const int64_t qrow = int64_t(qtile) * BS + wave * 32 + li;
   bf16x8 qf[D / 16];
   {
-    const __bf16* qsrc = qp + (bh * Lp + qrow) * D + 8 * g;
+    const __bf16* qsrc = qp + (bh * Lt + qrow) * D + 8 * g;
 #pragma unroll
-    for (int m = 0; m < D / 16; ++m) {
-      if (qrow < Lp) qf[m] = *reinterpret_cast<const bf16x8*>(qsrc + 16 * m);
-      else qf[m] = bf16x8{};
-    }
+    for (int m = 0; m < D / 16; ++m)
+      qf[m] = *reinterpret_cast<const bf16x8*>(qsrc + 16 * m);
   }
 
   f32x16 o[D / 32];
@@ -135,34 +161,33 @@ __global__ __launch_bounds__((BS / 32) * 64, 2) void attn_bf16_kernel(
   for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // Global -> LDS copies of one K and one V^T tile (global_load_lds_dwordx4:
-  // lane l of a wave instruction lands at LDS base + 16 l, so the LDS
-  // position is fixed and the swizzle is applied to the source chunk).
-  auto load_tile = [&](int32_t kt) {
-    const int64_t last = Lp - 1;
+  // Global -> LDS copies (global_load_lds_dwordx4: lane l of a wave
+  // instruction lands at LDS base + 16 l, so the LDS position is fixed and
+  // the swizzle is applied to the source chunk).  Addresses are a uniform
+  // tile base plus one 32-bit lane offset per variant.
+  uint32_t koff[KCopy::kVariants], voff[VCopy::kVariants];
+#pragma unroll
+  for (int u = 0; u < KCopy::kVariants; ++u) koff[u] = KCopy::lane_offset(wave, lane, u);
+#pragma unroll
+  for (int u = 0; u < VCopy::kVariants; ++u) voff[u] = VCopy::lane_offset(wave, lane, u);
+  auto load_k = [&](int32_t kt) {
+    const char* base = kh + int64_t(kt) * BS * C::kKRowBytes;
 #pragma unroll
     for (int u = 0; u < C::kKLoads; ++u) {
-      const int base = (u * C::kWaves + wave) * 64;   // first chunk of this instruction
-      const int pch = base + lane;
-      constexpr int CPR = C::kKRowBytes / 16;
-      const int r = pch / CPR, pc = pch % CPR;
-      const int gc = pc ^ swz<C::kKRowBytes>(r);
-      int64_t slot = int64_t(kt) * BS + r;
-      slot = slot < last ? slot : last;               // pad rows of a last text tile
+      const char* src = base + u * KCopy::kRowsPerCopy * C::kKRowBytes;
       __builtin_amdgcn_global_load_lds(
-          static_cast<const void*>(kh + slot * D + gc * 8),
-          (lds_void*)(ks + base * 8), 16, 0, 0);
+          (global_cvoid*)(src + koff[u % KCopy::kVariants]),
+          (lds_void*)(ks + (u * C::kWaves + wave) * 512), 16, 0, 0);
     }
+  };
+  auto load_v = [&](int32_t kt) {
+    const char* base = vh + int64_t(kt) * D * C::kVRowBytes;
 #pragma unroll
     for (int u = 0; u < C::kVLoads; ++u) {
-      const int base = (u * C::kWaves + wave) * 64;
-      const int pch = base + lane;
-      constexpr int CPR = C::kVRowBytes / 16;
-      const int r = pch / CPR, pc = pch % CPR;
-      const int gc = pc ^ swz<C::kVRowBytes>(r);
+      const char* src = base + u * VCopy::kRowsPerCopy * C::kVRowBytes;
       __builtin_amdgcn_global_load_lds(
-          static_cast<const void*>(vh + (int64_t(kt) * D + r) * BS + gc * 8),
-          (lds_void*)(vs + base * 8), 16, 0, 0);
+          (global_cvoid*)(src + voff[u % VCopy::kVariants]),
+          (lds_void*)(vs + (u * C::kWaves + wave) * 512), 16, 0, 0);
     }
   };
 
@@ -173,119 +198,140 @@ __global__ __launch_bounds__((BS / 32) * 64, 2) void attn_bf16_kernel(
   const int kswz = swz<C::kKRowBytes>(krow0);  // kb*32 does not change it
   const int vswz = swz<C::kVRowBytes>(li);     // nor does db*32
 
-  for (int it = 0; it < row_len; ++it) {
+  // Software pipeline over the kept tiles, one LDS buffer each for K and
+  // V^T.  Per tile t:
+  //   S(t) from K            | V(t) copies land (issued at the end of t-1)
+  //   barrier A: K free      -> issue K(t+1) copies
+  //   softmax(t)             | K(t+1) copies in flight
+  //   wait V(t); barrier B
+  //   P V(t) from V^T        | K(t+1) copies in flight
+  //   wait K(t+1); barrier C: V^T free -> issue V(t+1) copies
+  // Copies complete in issue order, so "wait until at most kKLoads copies
+  // are outstanding" means V(t) has landed.  The barriers are plain
+  // s_barrier after an LDS-read wait: they must not wait for the copies in
+  // flight, which a full fence would.
+  auto next_valid = [&](int i) {
+    while (i < row_len && (row[i] < 0 || row[i] >= n_tiles)) ++i;  // own bounds check
+    return i;
+  };
+  int it = next_valid(0);
+  if (it < row_len) {
+    load_k(row[it]);
+    load_v(row[it]);
+  }
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  while (it < row_len) {
     const int32_t kt = row[it];
-    if (kt < 0 || kt >= n_tiles) continue;            // uniform across the WG
-    __syncthreads();                                  // previous tile consumed
-    load_tile(kt);
-    __syncthreads();                                  // waits for the copies
+    const int nxt = next_valid(it + 1);
 
-    // The tile is processed in key groups of KG*32 keys (online softmax per
-    // group), which bounds the live S and P registers.
-    constexpr int KG = 1;
-    const bool full = tile_count[kt] == BS;
+    // S^T blocks: s[kb] covers keys kb*32 .. +32 (rows) x the wave's 32
+    // queries (columns).  MFMA row x of block kb is fed K row kb*32 +
+    // sigma(x), so accumulator register r = 4a + b of lane group g holds key
+    //   kb*32 + 16(a/2) + 8g + 4(a%2) + b,
+    // which makes the 8 keys behind registers 8h .. 8h+7 contiguous
+    // (kb*32 + 16h + 8g .. +8): the P V product then reads V^T with one
+    // 16-byte LDS access per operand.
+    f32x16 s[BS / 32];
 #pragma unroll
-    for (int grp = 0; grp < BS / 32 / KG; ++grp) {
-      // S^T blocks: s[j] covers keys (grp*KG + j)*32 .. +32 (rows) x the
-      // wave's 32 queries (columns).  MFMA row x of block kb is fed K row
-      // kb*32 + sigma(x), so accumulator register r = 4a + b of lane group g
-      // holds key
-      //   kb*32 + 16(a/2) + 8g + 4(a%2) + b,
-      // which makes the 8 keys behind registers 8h .. 8h+7 contiguous
-      // (kb*32 + 16h + 8g .. +8): the P V product then reads V^T with one
-      // 16-byte LDS access per operand.
-      f32x16 s[KG];
+    for (int kb = 0; kb < BS / 32; ++kb) {
+      s[kb] = f32x16{};
+      const __bf16* ka = ks + (kb * 32 + krow0) * D;
 #pragma unroll
-      for (int j = 0; j < KG; ++j) {
-        const int kb = grp * KG + j;
-        s[j] = f32x16{};
-        const __bf16* ka = ks + (kb * 32 + krow0) * D;
+      for (int m = 0; m < D / 16; ++m)
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            *reinterpret_cast<const bf16x8*>(ka + ((2 * m + g) ^ kswz) * 8), qf[m],
+            s[kb], 0, 0, 0);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // A
+    if (nxt < row_len) load_k(row[nxt]);
+
+    // Row max over the tile (raw dot products; the scale is positive).
+    float mx = -INFINITY;
+    if (tile_count[kt] == BS) {
 #pragma unroll
-        for (int m = 0; m < D / 16; ++m)
-          s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              *reinterpret_cast<const bf16x8*>(ka + ((2 * m + g) ^ kswz) * 8), qf[m],
-              s[j], 0, 0, 0);
-      }
-      // Row max over the group (raw dot products; the scale is positive).
-      float mx = -INFINITY;
-      if (full) {
+      for (int kb = 0; kb < BS / 32; ++kb)
 #pragma unroll
-        for (int j = 0; j < KG; ++j)
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    } else {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[j][r]);
-      } else {
+      for (int kb = 0; kb < BS / 32; ++kb) {
+        // Keys of lane group g sit at bit 8g + (16(a/2) + 4(a%2) + b).
+        const uint32_t bits = tile_bits[kt * 4 + kb] >> (8 * g);
 #pragma unroll
-        for (int j = 0; j < KG; ++j) {
-          const uint32_t bits = tile_bits[kt * 4 + grp * KG + j];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int a = r / 4, b = r % 4;
-            const int key = 16 * (a / 2) + 8 * g + 4 * (a % 2) + b;
-            const float x = ((bits >> key) & 1u) ? s[j][r] : -INFINITY;
-            s[j][r] = x;
-            mx = fmaxf(mx, x);
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int a = r / 4, b = r % 4;
+          const float x = ((bits >> (16 * (a / 2) + 4 * (a % 2) + b)) & 1u)
+                              ? s[kb][r] : -INFINITY;
+          s[kb][r] = x;
+          mx = fmaxf(mx, x);
         }
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      // Lazy rescaling: the running max only moves (and O, l are
-      // rescaled) when some query's group max exceeds it by more than 8 in
-      // log2 units; otherwise exponents stay below 2^8 relative to the
-      // stale max, which fp32 accumulation and bf16 P absorb.  The final
-      // 1/l uses the same reference, so the result is unchanged.  A group
-      // whose keys are all pad for this query gives mx = -inf and no move.
-      const float mt = mx * scale_log2;
-      if (__ballot(mt > m_run + 8.f) != 0) {
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // Lazy rescaling: the running max only moves (and O, l are rescaled)
+    // when some query's tile max exceeds it by more than 8 in log2 units;
+    // otherwise exponents stay below 2^8 relative to the stale max, which
+    // fp32 accumulation and bf16 P absorb.  The final 1/l uses the same
+    // reference, so the result is unchanged.
+    const float mt = mx * scale_log2;
+    if (__ballot(mt > m_run + 8.f) != 0) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
-      }
-      const float neg_m = -m_run;
-      float psum = 0.f;
-      bf16x8 pb[KG][2];
-#pragma unroll
-      for (int j = 0; j < KG; ++j) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          f32x8 p;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            p[e] = __builtin_amdgcn_exp2f(fmaf(s[j][8 * h + e], scale_log2, neg_m));
-            psum += p[e];
-          }
-          pb[j][h] = __builtin_convertvector(p, bf16x8);
-        }
-      }
-      l_run += psum;
+      for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+    }
+    const float neg_m = -m_run;
 
-      // O^T[db] += V^T[db rows, keys] P^T.  MFMA (kb, h): the k slots of
-      // lane group g are keys kb*32 + 16h + 8g .. +8 (see sigma above).
+    if (nxt < row_len) {
+      if constexpr (C::kKLoads == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else if constexpr (C::kKLoads == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    asm volatile("s_barrier" ::: "memory");                            // B
+
+    // Per 32-key block: P = exp2(S * scale - m) in bf16, then
+    // O^T[db] += V^T[db rows, keys] P^T; MFMA (kb, h) takes keys
+    // kb*32 + 16h + 8g .. +8 in lane group g (see sigma above).
+    float psum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < BS / 32; ++kb) {
+      bf16x8 pb[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        f32x8 p;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * h + e], scale_log2, neg_m));
+          psum[e % 4] += p[e];
+        }
+        pb[h] = __builtin_convertvector(p, bf16x8);
+      }
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
         const __bf16* va = vs + (db * 32 + li) * BS;
 #pragma unroll
-        for (int j = 0; j < KG; ++j) {
-          const int kb = grp * KG + j;
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                *reinterpret_cast<const bf16x8*>(va + ((4 * kb + 2 * h + g) ^ vswz) * 8),
-                pb[j][h], o[db], 0, 0, 0);
-        }
+        for (int h = 0; h < 2; ++h)
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              *reinterpret_cast<const bf16x8*>(va + ((4 * kb + 2 * h + g) ^ vswz) * 8),
+              pb[h], o[db], 0, 0, 0);
       }
     }
+    l_run += (psum[0] + psum[1]) + (psum[2] + psum[3]);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");  // C
+    if (nxt < row_len) load_v(row[nxt]);
+    it = nxt;
   }
 
   // Lane (li, g) holds O^T[dd = db*32 + 8a + 4g + b][query li].
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (qrow >= Lp) return;
   const int qs = wave * 32 + li;
   const bool qvalid = (tile_bits[qtile * 4 + qs / 32] >> (qs % 32)) & 1u;
   const float inv = (qvalid && l_tot > 0.f) ? 1.f / l_tot : 0.f;
-  __bf16* dst = op + (bh * Lp + qrow) * D + 4 * g;
+  __bf16* dst = op + (bh * Lt + qrow) * D + 4 * g;
   typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
@@ -305,7 +351,7 @@ __global__ __launch_bounds__(BS) void attn_f32_kernel(
     const float* __restrict__ qp, const float* __restrict__ kp,
     const float* __restrict__ vt, const int32_t* __restrict__ kept,
     float* __restrict__ op, const uint32_t* __restrict__ tile_bits,
-    const int32_t* __restrict__ tile_count, int64_t Lp, int32_t BH,
+    const int32_t* __restrict__ tile_count, int64_t Lt, int32_t BH,
     int32_t nb, int32_t n_tt, int32_t row_len_video, int64_t nnz,
     float scale) {
   // Keys are staged 32 at a time: K rows and V^T columns of one chunk.
@@ -317,7 +363,7 @@ __global__ __launch_bounds__(BS) void attn_f32_kernel(
   const int32_t qtile = job.tile;
   const int t = threadIdx.x;
   const int64_t qrow = int64_t(qtile) * BS + t;
-  const float* kh = kp + bh * Lp * D;
+  const float* kh = kp + bh * Lt * D;
   const float* vh = vt + bh * int64_t(n_tiles) * D * BS;
   const int32_t* row = kept + bh * nnz + row_offset(qtile, nb, row_len_video, n_tiles);
   const int32_t row_len = qtile < nb ? row_len_video : n_tiles;
@@ -325,7 +371,7 @@ __global__ __launch_bounds__(BS) void attn_f32_kernel(
   float q[D], o[D];
 #pragma unroll
   for (int c = 0; c < D; ++c) {
-    q[c] = qrow < Lp ? qp[(bh * Lp + qrow) * D + c] : 0.f;
+    q[c] = qp[(bh * Lt + qrow) * D + c];
     o[c] = 0.f;
   }
   float m_run = -INFINITY, l_run = 0.f;
@@ -338,7 +384,7 @@ __global__ __launch_bounds__(BS) void attn_f32_kernel(
       for (int c = t; c < 32 * D; c += BS) {
         const int r = c / D, cc = c % D;
         const int64_t slot = int64_t(kt) * BS + kc * 32 + r;
-        ks[r][cc] = slot < Lp ? kh[slot * D + cc] : 0.f;
+        ks[r][cc] = kh[slot * D + cc];
         const int vr = c / 32, vc = c % 32;
         vs[vr][vc] = vh[(int64_t(kt) * D + vr) * BS + kc * 32 + vc];
       }
@@ -375,10 +421,9 @@ __global__ __launch_bounds__(BS) void attn_f32_kernel(
       }
     }
   }
-  if (qrow >= Lp) return;
   const bool qvalid = (tile_bits[qtile * 4 + t / 32] >> (t % 32)) & 1u;
   const float inv = (qvalid && l_run > 0.f) ? 1.f / l_run : 0.f;
-  float* dst = op + (bh * Lp + qrow) * D;
+  float* dst = op + (bh * Lt + qrow) * D;
 #pragma unroll
   for (int c = 0; c < D; ++c) dst[c] = o[c] * inv;
 }
@@ -393,7 +438,7 @@ void launch_bf16(const rf_plan* p, const void* qp, const void* kp,
                      dim3(Bf16Cfg<D, BS>::kThreads), 0, st,
                      static_cast<const __bf16*>(qp), static_cast<const __bf16*>(kp),
                      static_cast<const __bf16*>(vt), kept, static_cast<__bf16*>(op),
-                     p->tile_bits, p->tile_count, p->sz.Lp, BH, nb, n_tt,
+                     p->tile_bits, p->tile_count, p->sz.Lt, BH, nb, n_tt,
                      kc.row_len_video, kc.nnz_per_head,
                      scale * 1.4426950408889634f);
 }
@@ -407,7 +452,7 @@ void launch_f32(const rf_plan* p, const void* qp, const void* kp,
   hipLaunchKernelGGL((attn_f32_kernel<D, BS>), grid, dim3(BS), 0, st,
                      static_cast<const float*>(qp), static_cast<const float*>(kp),
                      static_cast<const float*>(vt), kept, static_cast<float*>(op),
-                     p->tile_bits, p->tile_count, p->sz.Lp, BH, nb, n_tt,
+                     p->tile_bits, p->tile_count, p->sz.Lt, BH, nb, n_tt,
                      kc.row_len_video, kc.nnz_per_head, scale);
 }
 

@@ -18,7 +18,7 @@ __global__ __launch_bounds__(kThreads) void block_means_kernel(
     const uint8_t* __restrict__ qp, const uint8_t* __restrict__ kp,
     float* __restrict__ qbar, float* __restrict__ kbar,
     const uint32_t* __restrict__ tile_bits,
-    const int32_t* __restrict__ tile_count, int64_t Lp, int32_t nb) {
+    const int32_t* __restrict__ tile_count, int64_t Lt, int32_t nb) {
   constexpr int VE = 16 / E;          // elements per 16-byte chunk
   constexpr int CPR = D / VE;         // chunks per row
   constexpr int RG = kThreads / CPR;  // row groups
@@ -27,7 +27,7 @@ __global__ __launch_bounds__(kThreads) void block_means_kernel(
   const int blk = blockIdx.x;
   const int64_t bh = blockIdx.y;
   const uint8_t* src = (blockIdx.z == 0 ? qp : kp) +
-                       ((bh * Lp + int64_t(blk) * BS) * D) * E;
+                       ((bh * Lt + int64_t(blk) * BS) * D) * E;
   float* dst = (blockIdx.z == 0 ? qbar : kbar) + (bh * nb + blk) * D;
   const int k = threadIdx.x % CPR, rg = threadIdx.x / CPR;
   const uint32_t* bits = tile_bits + blk * 4;
@@ -71,7 +71,7 @@ void launch(const rf_plan* p, const void* qp, const void* kp, float* qbar,
   hipLaunchKernelGGL((block_means_kernel<E, D, BS>), grid, dim3(kThreads), 0,
                      st, static_cast<const uint8_t*>(qp),
                      static_cast<const uint8_t*>(kp), qbar, kbar, p->tile_bits,
-                     p->tile_count, p->sz.Lp, p->sz.nb);
+                     p->tile_count, p->sz.Lt, p->sz.nb);
 }
 
 }  // namespace

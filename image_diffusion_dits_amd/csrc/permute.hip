@@ -13,15 +13,15 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kChunksPerThread = 4;
 
-// xp[bh][s][:] = x[bh][slot_src[s]][:] (zeros for pad).  Grid: x over the
+// xp[bh][s][:] = x[bh][slot_src[s]][:] (zeros for pad), s < Lt.  Grid: x over the
 // chunks of one (b, h), y over b*H + h.
 __global__ __launch_bounds__(kThreads) void permute_rows_kernel(
     const uint4* __restrict__ x, uint4* __restrict__ xp,
-    const int32_t* __restrict__ slot_src, int32_t cpr, int64_t L, int64_t Lp) {
+    const int32_t* __restrict__ slot_src, int32_t cpr, int64_t L, int64_t Lt) {
   const int64_t bh = blockIdx.y;
-  const int32_t per_head = int32_t(Lp) * cpr;
+  const int32_t per_head = int32_t(Lt) * cpr;
   const uint4* src = x + bh * L * cpr;
-  uint4* dst = xp + bh * Lp * cpr;
+  uint4* dst = xp + bh * Lt * cpr;
   const int32_t base = blockIdx.x * (kThreads * kChunksPerThread) + threadIdx.x;
   uint4 v[kChunksPerThread];
 #pragma unroll
@@ -44,10 +44,10 @@ __global__ __launch_bounds__(kThreads) void permute_rows_kernel(
 // x[bh][n][:] = xp[bh][tok_slot[n]][:].
 __global__ __launch_bounds__(kThreads) void unpermute_rows_kernel(
     const uint4* __restrict__ xp, uint4* __restrict__ x,
-    const int32_t* __restrict__ tok_slot, int32_t cpr, int64_t L, int64_t Lp) {
+    const int32_t* __restrict__ tok_slot, int32_t cpr, int64_t L, int64_t Lt) {
   const int64_t bh = blockIdx.y;
   const int32_t per_head = int32_t(L) * cpr;
-  const uint4* src = xp + bh * Lp * cpr;
+  const uint4* src = xp + bh * Lt * cpr;
   uint4* dst = x + bh * L * cpr;
   const int32_t base = blockIdx.x * (kThreads * kChunksPerThread) + threadIdx.x;
   uint4 v[kChunksPerThread];
@@ -74,8 +74,7 @@ __global__ __launch_bounds__(kThreads) void unpermute_rows_kernel(
 template <int E, int D, int BS>
 __global__ __launch_bounds__(kThreads) void permute_tiles_t_kernel(
     const uint8_t* __restrict__ x, uint8_t* __restrict__ xt,
-    const int32_t* __restrict__ slot_src, int64_t L, int64_t Lp,
-    int32_t n_tiles) {
+    const int32_t* __restrict__ slot_src, int64_t L, int32_t n_tiles) {
   constexpr int VE = 16 / E;            // elements per chunk
   constexpr int CPR = D / VE;           // chunks per token row
   constexpr int ROW = D * E + 16;       // padded LDS row (bytes)
@@ -85,13 +84,10 @@ __global__ __launch_bounds__(kThreads) void permute_tiles_t_kernel(
   const uint8_t* src = x + bh * L * (D * E);
   for (int c = threadIdx.x; c < BS * CPR; c += kThreads) {
     const int s = c / CPR, k = c % CPR;
-    const int64_t slot = int64_t(tile) * BS + s;
+    const int32_t tok = slot_src[int64_t(tile) * BS + s];
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (slot < Lp) {
-      const int32_t tok = slot_src[slot];
-      if (tok >= 0)
-        v = *reinterpret_cast<const uint4*>(src + int64_t(tok) * (D * E) + k * 16);
-    }
+    if (tok >= 0)
+      v = *reinterpret_cast<const uint4*>(src + int64_t(tok) * (D * E) + k * 16);
     *reinterpret_cast<uint4*>(lds + s * ROW + k * 16) = v;
   }
   __syncthreads();
@@ -131,8 +127,7 @@ void launch_tiles_t(const rf_plan* p, const void* x, void* xt, int BH,
   dim3 grid(p->sz.n_tiles, BH);
   hipLaunchKernelGGL((permute_tiles_t_kernel<E, D, BS>), grid, dim3(kThreads),
                      0, st, static_cast<const uint8_t*>(x),
-                     static_cast<uint8_t*>(xt), p->slot_src, p->sz.L, p->sz.Lp,
-                     p->sz.n_tiles);
+                     static_cast<uint8_t*>(xt), p->slot_src, p->sz.L, p->sz.n_tiles);
 }
 
 }  // namespace
@@ -152,12 +147,12 @@ rf_status rf_permute(const rf_plan* plan, const void* x, void* xp, int32_t B,
   const int cpr = d * E / 16;
   const int BH = B * H;
   if (order == RF_ROWS) {
-    const int64_t per_head = plan->sz.Lp * cpr;
+    const int64_t per_head = plan->sz.Lt * cpr;
     dim3 grid((per_head + kThreads * kChunksPerThread - 1) /
                   (kThreads * kChunksPerThread), BH);
     hipLaunchKernelGGL(permute_rows_kernel, grid, dim3(kThreads), 0, stream,
                        static_cast<const uint4*>(x), static_cast<uint4*>(xp),
-                       plan->slot_src, cpr, plan->sz.L, plan->sz.Lp);
+                       plan->slot_src, cpr, plan->sz.L, plan->sz.Lt);
   } else {
     const int bs = plan->sz.bs;
     if (E == 2 && d == 128 && bs == 128) launch_tiles_t<2, 128, 128>(plan, x, xp, BH, stream);
@@ -185,7 +180,7 @@ rf_status rf_unpermute(const rf_plan* plan, const void* xp, void* x,
                 (kThreads * kChunksPerThread), B * H);
   hipLaunchKernelGGL(unpermute_rows_kernel, grid, dim3(kThreads), 0, stream,
                      static_cast<const uint4*>(xp), static_cast<uint4*>(x),
-                     plan->tok_slot, cpr, plan->sz.L, plan->sz.Lp);
+                     plan->tok_slot, cpr, plan->sz.L, plan->sz.Lt);
   return rf::check_launch("rf_unpermute");
 }
 

@@ -57,13 +57,14 @@ rf_status compute_sizes(const rf_layout* lay, rf_sizes* sz, Geometry* g) {
   const int64_t Np = nb * bs;
   const int64_t ntt = ceil_div(lay->n_text, bs);
   const int64_t Lp = Np + lay->n_text;
-  if (Lp >= (int64_t(1) << 31) - 256 || N >= (int64_t(1) << 31))
+  if ((nb + ntt) * bs >= (int64_t(1) << 31) - 256 || N >= (int64_t(1) << 31))
     return rf::fail(RF_ERR_INVALID_ARG, "sequence of %lld slots is too long",
                     (long long)Lp);
   sz->N = N;
   sz->Np = Np;
   sz->L = N + lay->n_text;
   sz->Lp = Lp;
+  sz->Lt = (nb + ntt) * bs;
   sz->bs = int32_t(bs);
   sz->nb = int32_t(nb);
   sz->n_text_tiles = int32_t(ntt);
@@ -96,7 +97,7 @@ struct HostTables {
 
 void build_tables(const rf_layout& lay, const rf_sizes& sz, const Geometry& g,
                   HostTables* t) {
-  t->slot_src.assign(sz.Lp, -1);
+  t->slot_src.assign(sz.Lt, -1);
   t->tok_slot.assign(sz.L, 0);
   t->tile_count.assign(sz.n_tiles, 0);
   t->tile_bits.assign(size_t(sz.n_tiles) * 4, 0u);
@@ -178,14 +179,14 @@ rf_status rf_layout_tables(const rf_layout* lay, int32_t* slot_src,
   if (st != RF_OK) return st;
   if (!slot_src || !tok_slot || !tile_count || !is_sink)
     return rf::fail(RF_ERR_INVALID_ARG, "rf_layout_tables: null buffer");
-  if (cap_slot_src < sz.Lp || cap_tok_slot < sz.L ||
+  if (cap_slot_src < sz.Lt || cap_tok_slot < sz.L ||
       cap_tile_count < sz.n_tiles || cap_is_sink < sz.nb)
     return rf::fail(RF_ERR_BUFFER_TOO_SMALL,
                     "rf_layout_tables: need %lld/%lld/%d/%d elements",
-                    (long long)sz.Lp, (long long)sz.L, sz.n_tiles, sz.nb);
+                    (long long)sz.Lt, (long long)sz.L, sz.n_tiles, sz.nb);
   HostTables t;
   build_tables(*lay, sz, g, &t);
-  memcpy(slot_src, t.slot_src.data(), sizeof(int32_t) * sz.Lp);
+  memcpy(slot_src, t.slot_src.data(), sizeof(int32_t) * sz.Lt);
   memcpy(tok_slot, t.tok_slot.data(), sizeof(int32_t) * sz.L);
   memcpy(tile_count, t.tile_count.data(), sizeof(int32_t) * sz.n_tiles);
   memcpy(is_sink, t.is_sink.data(), sz.nb);

@@ -29,7 +29,7 @@ class Layout(ctypes.Structure):
 
 class Sizes(ctypes.Structure):
     _fields_ = [("N", _c_i64), ("Np", _c_i64), ("L", _c_i64), ("Lp", _c_i64),
-                ("bs", _c_i32), ("nb", _c_i32), ("n_text_tiles", _c_i32),
+                ("Lt", _c_i64), ("bs", _c_i32), ("nb", _c_i32), ("n_text_tiles", _c_i32),
                 ("n_tiles", _c_i32), ("n_sink", _c_i32)]
 
     def as_dict(self):
@@ -125,7 +125,7 @@ def layout_tables(lay):
     """(slot_src, tok_slot, tile_count, is_sink) as numpy arrays."""
     lay = _as_layout(lay)
     z = layout_sizes(lay)
-    slot_src = np.empty(z["Lp"], np.int32)
+    slot_src = np.empty(z["Lt"], np.int32)
     tok_slot = np.empty(z["L"], np.int32)
     count = np.empty(z["n_tiles"], np.int32)
     sink = np.empty(z["nb"], np.uint8)
@@ -208,7 +208,7 @@ def permute(plan, x, order=ROWS, out=None):
         raise ValueError(f"x has {x.shape[2]} tokens, layout needs {z['L']}")
     if out is None:
         if order == ROWS:
-            out = torch.empty(B, H, z["Lp"], d, dtype=x.dtype, device=x.device)
+            out = torch.empty(B, H, z["Lt"], d, dtype=x.dtype, device=x.device)
         else:
             out = torch.empty(B, H, z["n_tiles"], d, z["bs"], dtype=x.dtype,
                               device=x.device)
@@ -220,8 +220,8 @@ def permute(plan, x, order=ROWS, out=None):
 def unpermute(plan, xp, out=None):
     B, H, d = _bhd(xp)
     z = plan.sizes
-    if xp.shape[2] != z["Lp"]:
-        raise ValueError(f"xp has {xp.shape[2]} slots, layout needs {z['Lp']}")
+    if xp.shape[2] != z["Lt"]:
+        raise ValueError(f"xp has {xp.shape[2]} slots, layout needs {z['Lt']}")
     if out is None:
         out = torch.empty(B, H, z["L"], d, dtype=xp.dtype, device=xp.device)
     _check(lib().rf_unpermute(plan.handle, _ptr(xp), _ptr(out), B, H, d,

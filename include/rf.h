@@ -27,7 +27,9 @@
  *   the N = T*H*W video tokens.  The permuted sequence has Np padded video
  *   slots (window order, pad slots zero) followed by the text tokens:
  *   Lp = Np + n_text slots.  Blocks ("tiles") are bs = wt*wh*ww consecutive
- *   slots: nb video blocks, then ceil(n_text/bs) text tiles.
+ *   slots: nb video blocks, then ceil(n_text/bs) text tiles.  Permuted
+ *   tensors hold whole tiles: Lt = n_tiles*bs rows, the rows after Lp (the
+ *   rest of a partial last text tile) being pad.
  *   Window order: blocks row-major over (frame, row, column) block
  *   coordinates of the grid padded up to whole windows; tokens row-major
  *   inside a block.  With permute = 0 the slots are the raster tokens and
@@ -63,7 +65,7 @@ typedef enum { RF_F32 = 0, RF_BF16 = 1 } rf_dtype;
 
 /* Order of a permuted tensor in memory. */
 typedef enum {
-  RF_ROWS = 0,    /* [B][H][Lp][d]: one row of d values per slot */
+  RF_ROWS = 0,    /* [B][H][Lt][d]: one row of d values per slot */
   RF_TILES_T = 1  /* [B][H][n_tiles][d][bs]: each tile transposed, the bs
                      slots of one feature contiguous (pad slots zero).  The
                      V operand of rf_sparse_attn uses this order. */
@@ -83,7 +85,8 @@ typedef struct {
   int64_t N;            /* video tokens T*H*W */
   int64_t Np;           /* padded video slots, nb*bs */
   int64_t L;            /* N + n_text: rows of an unpermuted tensor */
-  int64_t Lp;           /* Np + n_text: rows of a permuted RF_ROWS tensor */
+  int64_t Lp;           /* Np + n_text: slots holding video pad or tokens */
+  int64_t Lt;           /* n_tiles*bs: rows of a permuted RF_ROWS tensor */
   int32_t bs;           /* slots per block */
   int32_t nb;           /* video blocks */
   int32_t n_text_tiles; /* ceil(n_text / bs) */
@@ -112,7 +115,7 @@ rf_status rf_layout_sizes(const rf_layout* lay, rf_sizes* out);
 
 /* The plan's index tables, into caller-owned host buffers of the given
  * element capacities:
- *   slot_src[Lp]   raster token of each slot, -1 for pad;
+ *   slot_src[Lt]   raster token of each slot, -1 for pad;
  *   tok_slot[L]    slot of each raster token;
  *   tile_count[n_tiles]  valid slots per tile;
  *   is_sink[nb]    1 for sink blocks.
@@ -147,21 +150,21 @@ rf_status rf_plan_sizes(const rf_plan* plan, rf_sizes* out);
 
 /* 3D window permutation [RF2 Abstract insight (2); TL;DR; Figure 3].
  * x: [B][H][L][d] raster tokens (then text).  xp: permuted tensor in
- * `order` (RF_ROWS: [B][H][Lp][d]; RF_TILES_T: [B][H][n_tiles][d][bs]).
+ * `order` (RF_ROWS: [B][H][Lt][d]; RF_TILES_T: [B][H][n_tiles][d][bs]).
  * Pad slots are written as zeros.  dtype RF_BF16 or RF_F32; d in {64, 128}.
  * x and xp must not overlap. */
 rf_status rf_permute(const rf_plan* plan, const void* x, void* xp, int32_t B,
                      int32_t H, int32_t d, rf_dtype dtype, rf_order order,
                      hipStream_t stream);
 
-/* Inverse permutation: xp [B][H][Lp][d] (RF_ROWS) -> x [B][H][L][d]; pad
+/* Inverse permutation: xp [B][H][Lt][d] (RF_ROWS) -> x [B][H][L][d]; pad
  * slots are dropped, text rows copied back. */
 rf_status rf_unpermute(const rf_plan* plan, const void* xp, void* x,
                        int32_t B, int32_t H, int32_t d, rf_dtype dtype,
                        hipStream_t stream);
 
 /* Representative tokens [RF2 Abstract insight (1)]: the mean of each video
- * block's valid slots, accumulated in fp32.  qp, kp: [B][H][Lp][d]
+ * block's valid slots, accumulated in fp32.  qp, kp: [B][H][Lt][d]
  * (RF_ROWS; pad slots are ignored whatever they hold).  qbar, kbar:
  * fp32 [B][H][nb][d].  Text tiles are not pooled. */
 rf_status rf_block_means(const rf_plan* plan, const void* qp, const void* kp,
@@ -186,7 +189,7 @@ rf_status rf_predict_mask(const rf_plan* plan, const float* qbar,
  * insignificant tokens; RF1 review, Eq. (1)].  For each valid query slot of
  * tile i: o = sum_j softmax_j(scale * q . k_j) v_j over the valid slots of
  * the tiles listed in row i of kept_idx; pad query rows are written as 0.
- * qp, kp, op: [B][H][Lp][d] RF_ROWS; vt: [B][H][n_tiles][d][bs] RF_TILES_T.
+ * qp, kp, op: [B][H][Lt][d] RF_ROWS; vt: [B][H][n_tiles][d][bs] RF_TILES_T.
  * kept_idx as produced by rf_predict_mask for the same sparsity_pct; every
  * entry must lie in [0, n_tiles).  RF_BF16: bf16 operands, fp32
  * accumulation and softmax, bf16 output; RF_F32: fp32 throughout.

@@ -55,7 +55,9 @@ def test_host_tables_match_oracle(lay):
     assert np.array_equal(tok_slot[:oz["N"]], want_slot)
     assert np.array_equal(tok_slot[oz["N"]:], np.arange(oz["Np"], oz["Lp"]))
     valid = orc.slot_valid(o)
-    assert np.array_equal(slot_src >= 0, valid)
+    assert z["Lt"] == oz["n_tiles"] * oz["bs"] and len(slot_src) == z["Lt"]
+    assert np.array_equal(slot_src[:oz["Lp"]] >= 0, valid)
+    assert (slot_src[oz["Lp"]:] == -1).all()
     assert np.array_equal(slot_src[want_slot], np.arange(oz["N"]))
     assert np.array_equal(count[:oz["nb"]], orc.block_counts(o))
     want_sink = np.zeros(oz["nb"], np.uint8)
@@ -111,8 +113,8 @@ def test_invalid_layouts_return_status():
 def test_table_capacity_is_checked():
     L = rf.make_layout(**configs.TINY.layout)
     z = rf.layout_sizes(L)
-    small = np.empty(z["Lp"] - 1, np.int32)
-    ok = np.empty(max(z["Lp"], z["L"]), np.int32)
+    small = np.empty(z["Lt"] - 1, np.int32)
+    ok = np.empty(max(z["Lt"], z["L"]), np.int32)
     sink = np.empty(z["nb"], np.uint8)
     st_ = rf.lib().rf_layout_tables(ctypes.byref(L), small.ctypes.data, small.size,
                                     ok.ctypes.data, ok.size, ok.ctypes.data, ok.size,

@@ -51,7 +51,10 @@ def check_case(lay_dict, q, k, v, s, dtype, full_heads=None, sample_tiles=None,
     opb, ob = parity.bits(g["op"]), parity.bits(g["o"])
     qbar, kbar = parity.values(g["qbar"]), parity.values(g["kbar"])
     rows = rf.kept_rows(plan, g["kept"], s)
-    op = parity.values(g["op"])
+    Lp = z["Lp"]
+    op = parity.values(g["op"][:, :, :Lp])
+    for name in ("qp", "kp", "op"):        # whole-tile pad rows after Lp
+        assert torch.all(g[name][:, :, Lp:] == 0), name
     valid = orc.slot_valid(lay)
     rng = np.random.default_rng(seed)
     stats = dict(swaps=0, max_abs=0.0, mean_abs=[])
@@ -60,17 +63,17 @@ def check_case(lay_dict, q, k, v, s, dtype, full_heads=None, sample_tiles=None,
             sl = (slice(b, b + 1), slice(h, h + 1))
             # permutation, bit-exact
             qpo = orc.permute(qb[sl], lay)
-            assert np.array_equal(qpb[sl], qpo), f"Q permutation b{b} h{h}"
+            assert np.array_equal(qpb[sl][..., :Lp, :], qpo), f"Q permutation b{b} h{h}"
             kpo = orc.permute(kb[sl], lay)
-            assert np.array_equal(kpb[sl], kpo), f"K permutation b{b} h{h}"
+            assert np.array_equal(kpb[sl][..., :Lp, :], kpo), f"K permutation b{b} h{h}"
             vpo = orc.permute(vb[sl], lay)
             assert np.array_equal(vtb[sl], parity.tiles_t(vpo, lay)), \
                 f"V permutation b{b} h{h}"
-            assert np.array_equal(ob[sl], orc.unpermute(opb[sl], lay)), \
+            assert np.array_equal(ob[sl], orc.unpermute(opb[sl][..., :Lp, :], lay)), \
                 f"unpermutation b{b} h{h}"
             # means
-            qv = parity.values(g["qp"][b:b + 1, h:h + 1])
-            kv = parity.values(g["kp"][b:b + 1, h:h + 1])
+            qv = parity.values(g["qp"][b:b + 1, h:h + 1, :Lp])
+            kv = parity.values(g["kp"][b:b + 1, h:h + 1, :Lp])
             qbo, kbo = orc.block_means(qv, lay), orc.block_means(kv, lay)
             parity.check_means(qbar[sl], qbo)
             parity.check_means(kbar[sl], kbo)
@@ -142,8 +145,9 @@ def test_tiny_f32_workload():
     g, _ = check_case(cfg.layout, q, k, v, cfg.sparsity[0], "f32")
     # the optional logits equal the oracle's block scores
     lay = parity.olayout(cfg)
-    qbo = orc.block_means(parity.values(g["qp"]), lay)
-    kbo = orc.block_means(parity.values(g["kp"]), lay)
+    Lp = orc.sizes(lay)["Lp"]
+    qbo = orc.block_means(parity.values(g["qp"][:, :, :Lp]), lay)
+    kbo = orc.block_means(parity.values(g["kp"][:, :, :Lp]), lay)
     l, _ = orc.block_scores(qbo, kbo)
     np.testing.assert_allclose(parity.values(g["logits"]), l, atol=1e-6)
 
@@ -224,9 +228,11 @@ def test_out_of_range_kept_entries_are_skipped():
         got = rf.sparse_attn(plan, qp, kp, vt, bad, 0)
         torch.cuda.synchronize()
         rows = [[[np.array([0, 2, 3])] * z["n_tiles"]]]
-        want = orc.sparse_attention(parity.values(qp), parity.values(kp),
+        Lp = z["Lp"]
+        want = orc.sparse_attention(parity.values(qp[:, :, :Lp]),
+                                    parity.values(kp[:, :, :Lp]),
                                     orc.permute(parity.values(v), olay), rows, olay)
-        parity.check_attention(parity.values(got)[0, 0], want[0, 0],
+        parity.check_attention(parity.values(got)[0, 0, :Lp], want[0, 0],
                                orc.slot_valid(olay),
                                "bf16" if dt == torch.bfloat16 else "f32")
         assert not torch.equal(ref, got)
@@ -241,7 +247,7 @@ def test_gpu_argument_errors():
         rf.permute(plan, x[..., :48].contiguous())       # d = 48
     assert e.value.status == rf.ERR_UNSUPPORTED
     L = rf.lib()
-    xp = torch.zeros(1, 2, z["Lp"], 64, device="cuda")
+    xp = torch.zeros(1, 2, z["Lt"], 64, device="cuda")
     mis = x.view(-1)[1:].data_ptr()                     # 4-byte aligned only
     st = L.rf_permute(plan.handle, mis, xp.data_ptr(), 1, 2, 64, rf.F32,
                       rf.ROWS, None)
