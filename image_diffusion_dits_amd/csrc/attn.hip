@@ -198,18 +198,20 @@ __global__ __launch_bounds__((BS / 32) * 64, 2) void attn_bf16_kernel(
   const int kswz = swz<C::kKRowBytes>(krow0);  // kb*32 does not change it
   const int vswz = swz<C::kVRowBytes>(li);     // nor does db*32
 
-  // Software pipeline over the kept tiles, one LDS buffer each for K and
-  // V^T.  Per tile t:
-  //   S(t) from K            | V(t) copies land (issued at the end of t-1)
-  //   barrier A: K free      -> issue K(t+1) copies
-  //   softmax(t)             | K(t+1) copies in flight
-  //   wait V(t); barrier B
-  //   P V(t) from V^T        | K(t+1) copies in flight
-  //   wait K(t+1); barrier C: V^T free -> issue V(t+1) copies
-  // Copies complete in issue order, so "wait until at most kKLoads copies
-  // are outstanding" means V(t) has landed.  The barriers are plain
-  // s_barrier after an LDS-read wait: they must not wait for the copies in
-  // flight, which a full fence would.
+  // Schedule per kept tile t (one LDS buffer each for K and V^T):
+  //   S(t) = K(t) Q^T                      LDS reads, no copy in flight
+  //   barrier; copy K(t+1)
+  //   softmax(t) -> P(t)                   VALU, overlaps the K copy
+  //   wait copies; barrier
+  //   O^T += V^T(t) P^T(t)                 LDS reads, no copy in flight
+  //   barrier; copy V(t+1); wait; barrier
+  // Keeping copies out of the LDS-read phases keeps the compiler's LDS waits
+  // precise (with a copy pending they degrade to full drains); the V copy
+  // latency is covered by the other workgroup on the CU.  Waits use the
+  // s_waitcnt builtin so the compiler knows the copies have landed; the
+  // barriers are plain s_barrier.
+  constexpr int kWaitVm0 = 0x0F70;     // s_waitcnt vmcnt(0)
+  constexpr int kWaitLgkm0 = 0xC07F;   // s_waitcnt lgkmcnt(0)
   auto next_valid = [&](int i) {
     while (i < row_len && (row[i] < 0 || row[i] >= n_tiles)) ++i;  // own bounds check
     return i;
@@ -219,10 +221,24 @@ __global__ __launch_bounds__((BS / 32) * 64, 2) void attn_bf16_kernel(
     load_k(row[it]);
     load_v(row[it]);
   }
-  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __builtin_amdgcn_s_barrier();
   while (it < row_len) {
     const int32_t kt = row[it];
     const int nxt = next_valid(it + 1);
+    const int32_t kt_next = nxt < row_len ? row[nxt] : 0;
+    // Per-tile metadata is loaded here and forced complete before the LDS
+    // reads start: scalar loads in flight would also degrade the LDS waits.
+    const int32_t tcount = tile_count[kt];
+    uint32_t tbits[BS / 32];
+#pragma unroll
+    for (int kb = 0; kb < BS / 32; ++kb) tbits[kb] = tile_bits[kt * 4 + kb];
+    if constexpr (BS == 128)
+      asm volatile("" ::"s"(kt_next), "s"(tcount), "s"(tbits[0]), "s"(tbits[1]),
+                   "s"(tbits[2]), "s"(tbits[3]) : "memory");
+    else
+      asm volatile("" ::"s"(kt_next), "s"(tcount), "s"(tbits[0]), "s"(tbits[1])
+                   : "memory");
 
     // S^T blocks: s[kb] covers keys kb*32 .. +32 (rows) x the wave's 32
     // queries (columns).  MFMA row x of block kb is fed K row kb*32 +
@@ -242,12 +258,13 @@ __global__ __launch_bounds__((BS / 32) * 64, 2) void attn_bf16_kernel(
             *reinterpret_cast<const bf16x8*>(ka + ((2 * m + g) ^ kswz) * 8), qf[m],
             s[kb], 0, 0, 0);
     }
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // A
-    if (nxt < row_len) load_k(row[nxt]);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    if (nxt < row_len) load_k(kt_next);
 
     // Row max over the tile (raw dot products; the scale is positive).
     float mx = -INFINITY;
-    if (tile_count[kt] == BS) {
+    if (tcount == BS) {
 #pragma unroll
       for (int kb = 0; kb < BS / 32; ++kb)
 #pragma unroll
@@ -256,7 +273,7 @@ __global__ __launch_bounds__((BS / 32) * 64, 2) void attn_bf16_kernel(
 #pragma unroll
       for (int kb = 0; kb < BS / 32; ++kb) {
         // Keys of lane group g sit at bit 8g + (16(a/2) + 4(a%2) + b).
-        const uint32_t bits = tile_bits[kt * 4 + kb] >> (8 * g);
+        const uint32_t bits = tbits[kb] >> (8 * g);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int a = r / 4, b = r % 4;
@@ -283,23 +300,10 @@ __global__ __launch_bounds__((BS / 32) * 64, 2) void attn_bf16_kernel(
       for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
     }
     const float neg_m = -m_run;
-
-    if (nxt < row_len) {
-      if constexpr (C::kKLoads == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-      else if constexpr (C::kKLoads == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    asm volatile("s_barrier" ::: "memory");                            // B
-
-    // Per 32-key block: P = exp2(S * scale - m) in bf16, then
-    // O^T[db] += V^T[db rows, keys] P^T; MFMA (kb, h) takes keys
-    // kb*32 + 16h + 8g .. +8 in lane group g (see sigma above).
     float psum[4] = {0.f, 0.f, 0.f, 0.f};
+    bf16x8 pb[BS / 32][2];
 #pragma unroll
     for (int kb = 0; kb < BS / 32; ++kb) {
-      bf16x8 pb[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         f32x8 p;
@@ -308,8 +312,17 @@ __global__ __launch_bounds__((BS / 32) * 64, 2) void attn_bf16_kernel(
           p[e] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * h + e], scale_log2, neg_m));
           psum[e % 4] += p[e];
         }
-        pb[h] = __builtin_convertvector(p, bf16x8);
+        pb[kb][h] = __builtin_convertvector(p, bf16x8);
       }
+    }
+    l_run += (psum[0] + psum[1]) + (psum[2] + psum[3]);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __builtin_amdgcn_s_barrier();
+
+    // O^T[db] += V^T[db rows, keys] P^T; MFMA (kb, h) takes keys
+    // kb*32 + 16h + 8g .. +8 in lane group g (see sigma above).
+#pragma unroll
+    for (int kb = 0; kb < BS / 32; ++kb) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
         const __bf16* va = vs + (db * 32 + li) * BS;
@@ -317,12 +330,16 @@ __global__ __launch_bounds__((BS / 32) * 64, 2) void attn_bf16_kernel(
         for (int h = 0; h < 2; ++h)
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               *reinterpret_cast<const bf16x8*>(va + ((4 * kb + 2 * h + g) ^ vswz) * 8),
-              pb[h], o[db], 0, 0, 0);
+              pb[kb][h], o[db], 0, 0, 0);
       }
     }
-    l_run += (psum[0] + psum[1]) + (psum[2] + psum[3]);
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");  // C
-    if (nxt < row_len) load_v(row[nxt]);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    if (nxt < row_len) {
+      load_v(kt_next);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __builtin_amdgcn_s_barrier();
+    }
     it = nxt;
   }
 
