@@ -32,7 +32,71 @@ __device__ inline uint32_t order_key(float f) {
 
 __device__ inline int popc64(uint64_t m) { return __popcll(m); }
 
-template <int D, int R>
+// One wave selects one row: the k_sel largest keys among the non-sink
+// blocks (ties to the lower index), plus every sink, written ascending,
+// then the text tiles.  Lane l holds blocks l + 64 m (m < MMAX) in
+// registers as order-preserving keys, 0 for sinks and out-of-range blocks
+// (0 is below the key of every float, so they are never counted).
+//   tau: the largest t with #{key >= t} >= k_sel, found bit by bit from the
+//        top (wave ballots count); once #{key >= t} == k_sel exactly, the
+//        kept set is {key >= t} and the search stops.
+//   keep key > tau, and of the keys == tau the lowest-indexed
+//   k_sel - #{key > tau}; the ascending compaction is a ballot prefix count.
+template <int MMAX>
+__device__ void select_row(const float* __restrict__ row,
+                           const uint8_t* __restrict__ is_sink, int nb,
+                           int k_sel, int k_eff, int n_tt,
+                           int32_t* __restrict__ out, int lane) {
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint32_t key[MMAX];
+  uint32_t sinkm = 0;
+#pragma unroll
+  for (int m = 0; m < MMAX; ++m) {
+    const int j = lane + 64 * m;
+    key[m] = 0;
+    if (j < nb) {
+      if (is_sink[j]) sinkm |= 1u << m;
+      else key[m] = order_key(row[j]);
+    }
+  }
+  uint32_t tau = 0;
+  if (k_sel > 0) {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t t = tau | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int m = 0; m < MMAX; ++m) cnt += popc64(__ballot(key[m] >= t));
+      if (cnt >= k_sel) {
+        tau = t;
+        if (cnt == k_sel) break;
+      }
+    }
+  }
+  int n_gt = 0;
+  if (k_sel > 0) {
+#pragma unroll
+    for (int m = 0; m < MMAX; ++m) n_gt += popc64(__ballot(key[m] > tau));
+  }
+  const int n_eq_take = k_sel - n_gt;
+  int pos = 0, eq_seen = 0;
+#pragma unroll
+  for (int m = 0; m < MMAX; ++m) {
+    const int j = lane + 64 * m;
+    const bool sink = (sinkm >> m) & 1u;
+    const bool eq = k_sel > 0 && key[m] != 0 && key[m] == tau;
+    bool keep = sink || (k_sel > 0 && key[m] > tau);
+    const uint64_t eqm = __ballot(eq);
+    if (eq && eq_seen + popc64(eqm & lt_mask) < n_eq_take) keep = true;
+    eq_seen += popc64(eqm);
+    const uint64_t km = __ballot(keep);
+    const int at = pos + popc64(km & lt_mask);
+    if (keep && at < k_eff) out[at] = j;
+    pos += popc64(km);
+  }
+  for (int t = lane; t < n_tt; t += 64) out[k_eff + t] = nb + t;
+}
+
+template <int D, int R, int MMAX>
 __global__ __launch_bounds__(kThreads) void predict_mask_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar,
     const uint8_t* __restrict__ is_sink, int32_t* __restrict__ kept,
@@ -77,60 +141,12 @@ __global__ __launch_bounds__(kThreads) void predict_mask_kernel(
   __syncthreads();
 
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const int k_sel = k_eff - n_sink;
-  const int M = (nb + 63) / 64;
   for (int r = wave; r < R; r += kWaves) {
     const int i = i0 + r;
     if (i >= nb) break;
-    const float* row = sc + r * nb;
-    // Bisection for tau = the k_sel-th largest key among non-sink blocks.
-    uint32_t tau = 0;
-    if (k_sel > 0) {
-      for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t t = tau | (1u << bit);
-        int cnt = 0;
-        for (int m = 0; m < M; ++m) {
-          const int j = lane + 64 * m;
-          const bool ge = j < nb && !is_sink[j] && order_key(row[j]) >= t;
-          cnt += popc64(__ballot(ge));
-        }
-        if (cnt >= k_sel) tau = t;
-      }
-    }
-    // Keys above tau are kept; among keys equal to tau the lowest indices
-    // fill the remaining places.
-    int n_gt = 0;
-    if (k_sel > 0) {
-      for (int m = 0; m < M; ++m) {
-        const int j = lane + 64 * m;
-        n_gt += popc64(__ballot(j < nb && !is_sink[j] && order_key(row[j]) > tau));
-      }
-    }
-    const int n_eq_take = k_sel - n_gt;
-    int32_t* out = kept + bh * nnz + int64_t(i) * row_len;
-    int pos = 0, eq_seen = 0;
-    for (int m = 0; m < M; ++m) {
-      const int j = lane + 64 * m;
-      bool keep = false, eq = false;
-      if (j < nb) {
-        if (is_sink[j]) {
-          keep = true;
-        } else if (k_sel > 0) {
-          const uint32_t key = order_key(row[j]);
-          keep = key > tau;
-          eq = key == tau;
-        }
-      }
-      const uint64_t eqm = __ballot(eq);
-      if (eq && eq_seen + popc64(eqm & lt_mask) < n_eq_take) keep = true;
-      eq_seen += popc64(eqm);
-      const uint64_t km = __ballot(keep);
-      const int at = pos + popc64(km & lt_mask);
-      if (keep && at < k_eff) out[at] = j;
-      pos += popc64(km);
-    }
-    for (int t = lane; t < n_tt; t += 64) out[k_eff + t] = nb + t;
+    select_row<MMAX>(sc + r * nb, is_sink, nb, k_sel, k_eff, n_tt,
+                     kept + bh * nnz + int64_t(i) * row_len, lane);
   }
 }
 
@@ -144,17 +160,17 @@ __global__ void text_rows_kernel(int32_t* __restrict__ kept, int32_t nb,
   for (int t = threadIdx.x; t < n_tiles; t += blockDim.x) out[t] = t;
 }
 
-template <int D, int R>
+template <int D, int R, int MMAX>
 void launch(const rf_plan* p, const float* qbar, const float* kbar,
             int32_t* kept, float* logits, int BH, const rf_keep& kc,
             hipStream_t st) {
   const int nb = p->sz.nb;
   const size_t lds = sizeof(float) * (size_t(R) * D + size_t(R) * nb);
   (void)hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&predict_mask_kernel<D, R>),
+      reinterpret_cast<const void*>(&predict_mask_kernel<D, R, MMAX>),
       hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   dim3 grid((nb + R - 1) / R, BH);
-  hipLaunchKernelGGL((predict_mask_kernel<D, R>), grid, dim3(kThreads), lds, st,
+  hipLaunchKernelGGL((predict_mask_kernel<D, R, MMAX>), grid, dim3(kThreads), lds, st,
                      qbar, kbar, p->is_sink, kept, logits, nb, p->sz.n_sink,
                      kc.k_eff, p->sz.n_text_tiles, kc.row_len_video,
                      kc.nnz_per_head, 1.0f / sqrtf(float(D)));
@@ -180,15 +196,17 @@ extern "C" rf_status rf_predict_mask(const rf_plan* plan, const float* qbar,
   // Dots of R rows x nb blocks must fit in LDS next to the R query rows.
   const size_t budget = 128 * 1024;
   const int BH = B * H;
-  if (sizeof(float) * 16 * (size_t(nb) + d) <= budget) {
-    if (d == 128) launch<128, 16>(plan, qbar, kbar, kept_idx, logits_or_null, BH, kc, stream);
-    else launch<64, 16>(plan, qbar, kbar, kept_idx, logits_or_null, BH, kc, stream);
-  } else if (sizeof(float) * 4 * (size_t(nb) + d) <= budget) {
-    if (d == 128) launch<128, 4>(plan, qbar, kbar, kept_idx, logits_or_null, BH, kc, stream);
-    else launch<64, 4>(plan, qbar, kbar, kept_idx, logits_or_null, BH, kc, stream);
+  // Rows per workgroup R: their dots must fit in LDS next to the R query
+  // rows.  MMAX: register chunks per lane for the selection (nb <= 64 MMAX).
+  if (nb <= 1024 && sizeof(float) * 16 * (size_t(nb) + d) <= budget) {
+    if (d == 128) launch<128, 16, 16>(plan, qbar, kbar, kept_idx, logits_or_null, BH, kc, stream);
+    else launch<64, 16, 16>(plan, qbar, kbar, kept_idx, logits_or_null, BH, kc, stream);
+  } else if (nb <= 4096 && sizeof(float) * 4 * (size_t(nb) + d) <= budget) {
+    if (d == 128) launch<128, 4, 64>(plan, qbar, kbar, kept_idx, logits_or_null, BH, kc, stream);
+    else launch<64, 4, 64>(plan, qbar, kbar, kept_idx, logits_or_null, BH, kc, stream);
   } else {
     return rf::fail(RF_ERR_UNSUPPORTED, "rf_predict_mask: %d blocks per row "
-                    "exceed the LDS budget", nb);
+                    "exceed the supported maximum of 4096", nb);
   }
   if (plan->sz.n_text_tiles > 0) {
     dim3 grid(plan->sz.n_text_tiles, BH);

@@ -121,6 +121,80 @@ __global__ __launch_bounds__(kThreads) void permute_tiles_t_kernel(
   }
 }
 
+// Permutation fused with block-mean pooling: one workgroup per
+// (tile, b*H + h) gathers the tile's BS rows, writes them contiguously and,
+// for video blocks, accumulates each feature over the valid slots (fp32,
+// fixed order) and writes the mean.  The pooling then costs no extra HBM
+// pass.  Text tiles are only copied.
+template <int E, int D, int BS>
+__global__ __launch_bounds__(kThreads) void permute_means_kernel(
+    const uint8_t* __restrict__ x, uint8_t* __restrict__ xp,
+    float* __restrict__ xbar, const int32_t* __restrict__ slot_src,
+    const int32_t* __restrict__ tile_count, int64_t L, int64_t Lt,
+    int32_t nb) {
+  constexpr int VE = 16 / E;            // elements per 16-byte chunk
+  constexpr int CPR = D / VE;           // chunks per row
+  constexpr int RG = kThreads / CPR;    // row groups
+  static_assert(RG >= 1 && BS % RG == 0, "layout");
+  __shared__ float part[RG][D];
+  const int64_t bh = blockIdx.y;
+  const int32_t tile = blockIdx.x;
+  const uint8_t* src = x + bh * L * (D * E);
+  uint8_t* dst = xp + (bh * Lt + int64_t(tile) * BS) * (D * E);
+  const int k = threadIdx.x % CPR, rg = threadIdx.x / CPR;
+  float acc[VE];
+#pragma unroll
+  for (int e = 0; e < VE; ++e) acc[e] = 0.f;
+  uint4 v[BS / RG];
+#pragma unroll
+  for (int i = 0; i < BS / RG; ++i) {
+    const int s = rg + i * RG;
+    const int32_t tok = slot_src[int64_t(tile) * BS + s];
+    v[i] = make_uint4(0, 0, 0, 0);
+    if (tok >= 0)
+      v[i] = *reinterpret_cast<const uint4*>(src + int64_t(tok) * (D * E) + k * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < BS / RG; ++i) {
+    const int s = rg + i * RG;
+    *reinterpret_cast<uint4*>(dst + int64_t(s) * (D * E) + k * 16) = v[i];
+    // Pad slots hold zeros here, so summing every slot sums the valid ones.
+    if constexpr (E == 2) {
+      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += __uint_as_float(w[e] << 16);
+        acc[2 * e + 1] += __uint_as_float(w[e] & 0xffff0000u);
+      }
+    } else {
+      acc[0] += __uint_as_float(v[i].x);
+      acc[1] += __uint_as_float(v[i].y);
+      acc[2] += __uint_as_float(v[i].z);
+      acc[3] += __uint_as_float(v[i].w);
+    }
+  }
+  if (tile >= nb) return;                       // text: copy only (uniform)
+#pragma unroll
+  for (int e = 0; e < VE; ++e) part[rg][k * VE + e] = acc[e];
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float sum = 0.f;
+#pragma unroll
+    for (int r = 0; r < RG; ++r) sum += part[r][threadIdx.x];
+    xbar[(bh * nb + tile) * D + threadIdx.x] = sum / float(tile_count[tile]);
+  }
+}
+
+template <int E, int D, int BS>
+void launch_means(const rf_plan* p, const void* x, void* xp, float* xbar,
+                  int BH, hipStream_t st) {
+  dim3 grid(p->sz.n_tiles, BH);
+  hipLaunchKernelGGL((permute_means_kernel<E, D, BS>), grid, dim3(kThreads), 0, st,
+                     static_cast<const uint8_t*>(x), static_cast<uint8_t*>(xp),
+                     xbar, p->slot_src, p->tile_count, p->sz.L, p->sz.Lt,
+                     p->sz.nb);
+}
+
 template <int E, int D, int BS>
 void launch_tiles_t(const rf_plan* p, const void* x, void* xt, int BH,
                     hipStream_t st) {
@@ -165,6 +239,27 @@ rf_status rf_permute(const rf_plan* plan, const void* x, void* xp, int32_t B,
     else launch_tiles_t<4, 64, 64>(plan, x, xp, BH, stream);
   }
   return rf::check_launch("rf_permute");
+}
+
+rf_status rf_permute_means(const rf_plan* plan, const void* x, void* xp,
+                           float* xbar, int32_t B, int32_t H, int32_t d,
+                           rf_dtype dtype, hipStream_t stream) {
+  rf_status st = rf::check_call(plan, B, H, d, dtype, "rf_permute_means");
+  if (st != RF_OK) return st;
+  if (!rf::aligned16(x) || !rf::aligned16(xp) || !rf::aligned16(xbar))
+    return rf::fail(RF_ERR_INVALID_ARG, "rf_permute_means: null or misaligned buffer");
+  const int BH = B * H;
+  const int bs = plan->sz.bs;
+  const bool bf = dtype == RF_BF16;
+  if (bf && d == 128 && bs == 128) launch_means<2, 128, 128>(plan, x, xp, xbar, BH, stream);
+  else if (bf && d == 128 && bs == 64) launch_means<2, 128, 64>(plan, x, xp, xbar, BH, stream);
+  else if (bf && d == 64 && bs == 128) launch_means<2, 64, 128>(plan, x, xp, xbar, BH, stream);
+  else if (bf && d == 64 && bs == 64) launch_means<2, 64, 64>(plan, x, xp, xbar, BH, stream);
+  else if (!bf && d == 128 && bs == 128) launch_means<4, 128, 128>(plan, x, xp, xbar, BH, stream);
+  else if (!bf && d == 128 && bs == 64) launch_means<4, 128, 64>(plan, x, xp, xbar, BH, stream);
+  else if (!bf && d == 64 && bs == 128) launch_means<4, 64, 128>(plan, x, xp, xbar, BH, stream);
+  else launch_means<4, 64, 64>(plan, x, xp, xbar, BH, stream);
+  return rf::check_launch("rf_permute_means");
 }
 
 rf_status rf_unpermute(const rf_plan* plan, const void* xp, void* x,

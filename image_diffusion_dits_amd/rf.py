@@ -60,6 +60,8 @@ _SIGNATURES = {
     "rf_plan_sizes": [_vp, _P(Sizes)],
     "rf_permute": [_vp, _vp, _vp, _c_i32, _c_i32, _c_i32, ctypes.c_int,
                    ctypes.c_int, _vp],
+    "rf_permute_means": [_vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32,
+                         ctypes.c_int, _vp],
     "rf_unpermute": [_vp, _vp, _vp, _c_i32, _c_i32, _c_i32, ctypes.c_int, _vp],
     "rf_block_means": [_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32,
                        ctypes.c_int, _vp],
@@ -217,6 +219,22 @@ def permute(plan, x, order=ROWS, out=None):
     return out
 
 
+def permute_means(plan, x, out=None, xbar=None):
+    """Permuted rows of x (RF_ROWS) and the block means, in one pass."""
+    B, H, d = _bhd(x)
+    z = plan.sizes
+    if x.shape[2] != z["L"]:
+        raise ValueError(f"x has {x.shape[2]} tokens, layout needs {z['L']}")
+    if out is None:
+        out = torch.empty(B, H, z["Lt"], d, dtype=x.dtype, device=x.device)
+    if xbar is None:
+        xbar = torch.empty(B, H, z["nb"], d, dtype=torch.float32, device=x.device)
+    _check(lib().rf_permute_means(plan.handle, _ptr(x), _ptr(out), _ptr(xbar), B,
+                                  H, d, _dtype_code(x), _stream()),
+           "rf_permute_means")
+    return out, xbar
+
+
 def unpermute(plan, xp, out=None):
     B, H, d = _bhd(xp)
     z = plan.sizes
@@ -296,10 +314,9 @@ def kept_rows(plan, kept, sparsity_pct):
 def sparse_attention(q, k, v, plan, sparsity_pct, scale=None):
     """The whole path on raster tensors [B, H, N + n_text, d]: permute,
     pool, predict, attend, unpermute.  Returns (o, kept)."""
-    qp = permute(plan, q)
-    kp = permute(plan, k)
+    qp, qbar = permute_means(plan, q)
+    kp, kbar = permute_means(plan, k)
     vt = permute(plan, v, order=TILES_T)
-    qbar, kbar = block_means(plan, qp, kp)
     kept = predict_mask(plan, qbar, kbar, sparsity_pct)
     op = sparse_attn(plan, qp, kp, vt, kept, sparsity_pct, scale=scale)
     return unpermute(plan, op), kept

@@ -17,6 +17,7 @@
  * stream:
  *   rf_permute(Q), rf_permute(K), rf_permute(V, RF_TILES_T)   3D windows
  *   rf_block_means(Qp, Kp)                                     Qbar, Kbar
+ *     (or rf_permute_means(Q), rf_permute_means(K): both in one pass)
  *   rf_predict_mask(Qbar, Kbar)                                kept tiles
  *   rf_sparse_attn(Qp, Kp, Vt, kept)                           Op
  *   rf_unpermute(Op)                                           O
@@ -156,6 +157,14 @@ rf_status rf_plan_sizes(const rf_plan* plan, rf_sizes* out);
 rf_status rf_permute(const rf_plan* plan, const void* x, void* xp, int32_t B,
                      int32_t H, int32_t d, rf_dtype dtype, rf_order order,
                      hipStream_t stream);
+
+/* rf_permute (RF_ROWS) fused with rf_block_means on the same tensor: the
+ * permuted rows of x go to xp and the mean of each video block's valid
+ * slots [RF2 Abstract insight (1)] to xbar, fp32 [B][H][nb][d], in one
+ * pass over x.  Same arguments and errors as rf_permute. */
+rf_status rf_permute_means(const rf_plan* plan, const void* x, void* xp,
+                           float* xbar, int32_t B, int32_t H, int32_t d,
+                           rf_dtype dtype, hipStream_t stream);
 
 /* Inverse permutation: xp [B][H][Lt][d] (RF_ROWS) -> x [B][H][L][d]; pad
  * slots are dropped, text rows copied back. */

@@ -24,10 +24,9 @@ def say(*a):
 
 
 def run_gpu(plan, q, k, v, s, logits=False):
-    qp = rf.permute(plan, q)
-    kp = rf.permute(plan, k)
+    qp, qbar = rf.permute_means(plan, q)
+    kp, kbar = rf.permute_means(plan, k)
     vt = rf.permute(plan, v, order=rf.TILES_T)
-    qbar, kbar = rf.block_means(plan, qp, kp)
     kept, lg = rf.predict_mask(plan, qbar, kbar, s, logits=True)
     op = rf.sparse_attn(plan, qp, kp, vt, kept, s)
     o = rf.unpermute(plan, op)
@@ -45,6 +44,14 @@ def check_case(lay_dict, q, k, v, s, dtype, full_heads=None, sample_tiles=None,
     z = orc.sizes(lay)
     plan = rf.Plan(lay_dict)
     g = gpu if gpu is not None else run_gpu(plan, q, k, v, s)
+    # The unfused entry points give the same bytes as the fused one.
+    qp2, kp2 = rf.permute(plan, q), rf.permute(plan, k)
+    qbar2, kbar2 = rf.block_means(plan, qp2, kp2)
+    torch.cuda.synchronize()
+    assert torch.equal(qp2, g["qp"]) and torch.equal(kp2, g["kp"])
+    torch.testing.assert_close(qbar2, g["qbar"], rtol=1e-6, atol=1e-7)
+    torch.testing.assert_close(kbar2, g["kbar"], rtol=1e-6, atol=1e-7)
+    del qp2, kp2, qbar2, kbar2
     B, H = q.shape[:2]
     qb, kb, vb = parity.bits(q), parity.bits(k), parity.bits(v)
     qpb, kpb, vtb = parity.bits(g["qp"]), parity.bits(g["kp"]), parity.bits(g["vt"])
