@@ -245,7 +245,7 @@ def main():
             "unpermute": round(unperm_bytes / (stage_ms["unpermute"] / 1e3) / 1e9, 1),
         },
         "roofline": {
-            "kernel": "attn_bf16_kernel" if cfg.dtype == "bf16" else "attn_f32_kernel",
+            "kernel": "attn_bf16_pp_kernel" if cfg.dtype == "bf16" else "attn_f32_kernel",
             "bound": "mfma",
             "achieved": round(attn_tflops, 2),
             "peak": peak,

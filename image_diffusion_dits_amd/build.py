@@ -30,6 +30,14 @@ COMMON = [
 ]
 
 
+# Per-source extra flags.  The attention kernels pin their output
+# accumulators to AGPRs explicitly; every other MFMA result (the score tiles
+# the softmax reads) is kept in VGPRs.
+EXTRA = {
+    "attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
                   if f.endswith((".hip", ".cpp")))
@@ -37,7 +45,8 @@ def sources():
 
 def _compile(src, verbose):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, "-x", "hip", "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(os.path.basename(src), []), "-x", "hip",
+           "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -3,8 +3,7 @@
 // sparse attention; RainFusion review page, Assumptions: softmax attention,
 // Eq. (1)).
 //
-// bf16 path (gfx950 MFMA).  One workgroup per (b, h, query tile) with one
-// wave per 32 queries.  Per kept key tile:
+// bf16 path (gfx950 MFMA), one wave per 32 queries.  Per kept key tile:
 //   S^T = K Q^T       v_mfma_f32_32x32x16_bf16, A = K rows from LDS,
 //                     B = the wave's Q held in registers for the whole row;
 //   online softmax    in fp32 registers; in the S^T accumulator layout each
@@ -15,17 +14,23 @@
 //                     done here), B = P^T taken straight from the S^T
 //                     accumulators converted to bf16;
 // and O^T's accumulator layout again gives each lane one query column, so
-// the softmax rescale is a per-lane scalar.  K and V^T tiles are staged in
-// padded LDS rows (conflict-free 16-byte / 8-byte reads), the next tile's
-// global loads are issued before the current tile's math.  Pad keys get
-// -inf from the plan's per-tile validity masks; pad query rows are written
-// as zeros.  Workgroups are renumbered so that each XCD (one L2) works on a
-// contiguous range of query tiles of one head; the heavy text query tiles
-// (which keep every tile) start first.
+// the softmax rescale is a per-lane scalar.  K and V^T tiles are copied into
+// XOR-swizzled LDS rows by LDS DMA (conflict-free 16-byte reads).  Pad keys
+// get -inf from the plan's per-tile validity masks; pad query rows are
+// written as zeros.  Workgroups are renumbered so that each XCD (one L2)
+// works on a contiguous range of query tiles of one head; the heavy text
+// query tiles (which keep every tile) start first.
+//
+// For 128-slot tiles the ping-pong kernel runs two groups of four waves per
+// query tile, one phase apart, so that MFMA and softmax work of the two
+// waves on each SIMD overlap (attn_bf16_pp_kernel); 64-slot tiles use one
+// group of waves that alternates the phases itself (attn_bf16_kernel).
 //
 // fp32 path: one thread per query row, fp32 FMA and expf, the same tile
 // walk; used where fp32 accuracy is required.
 #include "rf_internal.h"
+
+#include <type_traits>
 
 namespace {
 
@@ -33,6 +38,7 @@ typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x8 __attribute__((__vector_size__(8 * sizeof(float))));
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
 
 constexpr int kXcds = 8;
 
@@ -361,6 +367,343 @@ __global__ __launch_bounds__((BS / 32) * 64, 2) void attn_bf16_kernel(
   }
 }
 
+// ------------------------------- bf16 MFMA, ping-pong over two wave groups
+
+// One workgroup of eight waves per query tile of 128 slots, one workgroup per
+// CU.  Waves w and w + 4 share a SIMD; both hold the same 32 queries.  Group
+// 0 (waves 0-3) walks the even entries of the kept row, group 1 the odd
+// ones, each with its own K and V^T tile in LDS and its own softmax state.
+// Work alternates between two phases separated by workgroup barriers:
+//   MFMA phase of tile i:  O^T += V^T(i-1) P^T(i-1), then S(i) = K(i) Q^T
+//   VALU phase of tile i:  copies of K(i+1) and V^T(i); softmax(i) -> P(i)
+// and the groups are one phase apart, so on every SIMD one wave issues
+// MFMAs while the other runs its softmax: the matrix core and the vector
+// ALU work at the same time by construction.  The copies of a group land
+// during its own VALU phase.  At the end group 1 hands its O, m and l to
+// group 0 through LDS and group 0 merges and stores.
+template <int D>
+struct PpCfg {
+  static constexpr int BS = 128;
+  static constexpr int kGroupWaves = 4;                 // one per SIMD
+  static constexpr int kThreads = 2 * kGroupWaves * 64;
+  static constexpr int kKRowBytes = D * 2;              // K row (LDS and global)
+  static constexpr int kVRowBytes = BS * 2;             // V^T row (LDS and global)
+  static constexpr int kTileBytes = BS * D * 2;         // K or V^T tile
+  static constexpr int kTileElems = BS * D;
+  static constexpr int kCopies = kTileBytes / 16 / (kGroupWaves * 64);   // per thread
+  static_assert(kCopies * 16 * kGroupWaves * 64 == kTileBytes, "copy split");
+};
+
+// XOR swizzle of the 16-byte chunks of LDS rows of RB bytes: the 16 rows
+// read by one ds_read_b128 phase (one chunk column of 16 consecutive rows,
+// or the sigma image of them) land on 16 distinct bank groups.
+template <int RB>
+__device__ inline int swz_rows(int r) {
+  return (r / (256 / RB)) % (RB / 16);
+}
+
+// Byte offset, inside a tile with LDS rows of RB bytes (global rows GROW
+// bytes apart), of the 16-byte chunk that lane `lane` of group wave `w`
+// moves in copy 0: the copy writes LDS bytes [w * 1024, +1024), so lane l
+// lands on LDS chunk q = w*64 + l: row q / (RB/16), position q % (RB/16),
+// which holds global chunk position ^ swizzle.  Copy u moves the rows
+// u * WAVES * 64 / (RB/16) further on, a multiple of 16, so the swizzle and
+// the lane offset are the same for every copy.
+template <int RB, int GROW, int WAVES>
+__device__ inline uint32_t dma_offset(int w, int lane) {
+  constexpr int cpr = RB / 16;
+  static_assert((WAVES * 64 / cpr) % 16 == 0, "copy-invariant swizzle");
+  const int q = w * 64 + lane;
+  const int r = q / cpr, pc = q % cpr;
+  return uint32_t(r * GROW + (pc ^ swz_rows<RB>(r)) * 16);
+}
+
+// Word 3 of a raw buffer resource (untyped dword access) on gfx9-family
+// GPUs.
+constexpr int kBufferWord3 = 0x00020000;
+
+// Copies one tile of `bytes` bytes at `base` into LDS at `dst` through a
+// buffer resource spanning exactly the tile: copy u of group wave w writes
+// LDS [dst + (u*WAVES + w) * 1024, +1024) from lane offset voff + u * the
+// bytes one copy covers.
+template <int COPIES, int WAVES>
+__device__ __forceinline__ void dma_tile(const char* base, int bytes, __bf16* dst,
+                                         uint32_t voff, int w) {
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, bytes, kBufferWord3);
+  constexpr int kStride = WAVES * 64 * 16;
+#pragma unroll
+  for (int u = 0; u < COPIES; ++u)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, (lds_void*)(dst + (u * WAVES + w) * 512), 16, voff, u * kStride, 0, 0);
+}
+
+template <int D>
+__global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
+    const __bf16* __restrict__ qp, const __bf16* __restrict__ kp,
+    const __bf16* __restrict__ vt, const int32_t* __restrict__ kept,
+    __bf16* __restrict__ op, const uint32_t* __restrict__ tile_bits,
+    const int32_t* __restrict__ tile_count, int64_t Lt, int32_t BH,
+    int32_t nb, int32_t n_tt, int32_t row_len_video, int64_t nnz,
+    float scale_log2) {
+  using C = PpCfg<D>;
+  constexpr int BS = C::BS;
+  constexpr int kWaitVm0 = 0x0F70;     // s_waitcnt vmcnt(0)
+  // K and V^T tiles of group 0, then of group 1; reused for the merge.
+  __shared__ __align__(16) __bf16 lds[4 * C::kTileElems];
+  __shared__ float m_buf[C::kGroupWaves * 64], l_buf[C::kGroupWaves * 64];
+
+  const int32_t n_tiles = nb + n_tt;
+  const TileJob job = job_of(blockIdx.x, BH, nb, n_tt);
+  const int64_t bh = job.bh;
+  const int32_t qtile = job.tile;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  const int grp = wave / C::kGroupWaves;
+  const int qw = wave % C::kGroupWaves;
+  const int lane = threadIdx.x % 64;
+  const int li = lane % 32, g = lane / 32;
+  __bf16* const ks = lds + (2 * grp) * C::kTileElems;
+  __bf16* const vs = lds + (2 * grp + 1) * C::kTileElems;
+
+  const char* kh = reinterpret_cast<const char*>(kp + bh * Lt * D);
+  const char* vh = reinterpret_cast<const char*>(vt + bh * int64_t(n_tiles) * D * BS);
+  const __attribute__((address_space(4))) int32_t* row =
+      (const __attribute__((address_space(4))) int32_t*)(
+          kept + bh * nnz + row_offset(qtile, nb, row_len_video, n_tiles));
+  const int32_t row_len = qtile < nb ? row_len_video : n_tiles;
+  const int32_t n_grp = (row_len + 1) / 2;   // tiles per group; group 1 may end on a masked one
+  // Kept tile of this group's tile i, or -1: entries past the end and ids out
+  // of range are walked as fully masked tiles (whose copies read tile 0).
+  auto tile_of = [&](int32_t i) -> int32_t {
+    const int32_t j = 2 * i + grp;
+    const int32_t kt = row[min(j, row_len - 1)];
+    return (j < row_len && kt >= 0 && kt < n_tiles) ? kt : -1;
+  };
+
+  // Q operand (B of S^T = K Q^T): lane (li, g) holds q[li][16m + 8g .. +8].
+  const int64_t qrow = int64_t(qtile) * BS + qw * 32 + li;
+  bf16x8 qf[D / 16];
+  {
+    const __bf16* qsrc = qp + (bh * Lt + qrow) * D + 8 * g;
+#pragma unroll
+    for (int m = 0; m < D / 16; ++m)
+      qf[m] = *reinterpret_cast<const bf16x8*>(qsrc + 16 * m);
+  }
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 s[BS / 32];
+  bf16x8 pb[BS / 32][2];
+
+  const uint32_t koff = dma_offset<C::kKRowBytes, C::kKRowBytes, C::kGroupWaves>(qw, lane);
+  const uint32_t voff = dma_offset<C::kVRowBytes, C::kVRowBytes, C::kGroupWaves>(qw, lane);
+  auto copy_k = [&](int32_t kt) {
+    dma_tile<C::kCopies, C::kGroupWaves>(kh + int64_t(max(kt, 0)) * C::kTileBytes,
+                                         C::kTileBytes, ks, koff, qw);
+  };
+  auto copy_v = [&](int32_t kt) {
+    dma_tile<C::kCopies, C::kGroupWaves>(vh + int64_t(max(kt, 0)) * C::kTileBytes,
+                                         C::kTileBytes, vs, voff, qw);
+  };
+
+  // LDS element offsets of this lane's operand chunks.
+  //   K (A of S^T): row kb*32 + sigma(li), chunk 2m + g.
+  //   V^T (A of O^T): row db*32 + li, chunk 4kb + 2h + g.
+  const int krow0 = sigma(li);
+  const int kswz = swz_rows<C::kKRowBytes>(krow0);  // kb*32 does not change it
+  const int vswz = swz_rows<C::kVRowBytes>(li);     // nor does db*32
+
+  // Instruction order of one block of 32 operand reads and 32 MFMAs: the
+  // reads run kAhead MFMAs ahead of their use, so LDS latency is covered
+  // inside the wave (the other wave on the SIMD is in its VALU phase).
+  constexpr int kAhead = 8;
+  constexpr int kBlockMfma = BS / 32 * D / 16;   // 32 for D = 128
+  auto pipeline_reads = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);        // DS reads
+#pragma unroll
+    for (int j = 0; j < kBlockMfma - kAhead; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);           // DS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
+  };
+
+  // MFMA phase of tile i.
+  auto mfma_phase = [&](int32_t i) {
+    if (i >= 1) {
+      // O^T[db] += V^T[db rows, keys] P^T(i-1); MFMA (kb, h) takes keys
+      // kb*32 + 16h + 8g .. +8 in lane group g.
+#pragma unroll
+      for (int kb = 0; kb < BS / 32; ++kb) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const __bf16* va = vs + (db * 32 + li) * BS;
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                *reinterpret_cast<const bf16x8*>(va + ((4 * kb + 2 * h + g) ^ vswz) * 8),
+                pb[kb][h], o[db], 0, 0, 0);
+        }
+      }
+      pipeline_reads();
+    }
+    // P(i-1) dies with the PV above before the scores of tile i are born.
+    __builtin_amdgcn_sched_barrier(0);
+    if (i < n_grp) {
+      // S^T blocks: s[kb] covers keys kb*32 .. +32 x the wave's 32 queries.
+      // MFMA row x of block kb is fed K row kb*32 + sigma(x), so
+      // accumulator register r = 4a + b of lane group g holds key
+      //   kb*32 + 16(a/2) + 8g + 4(a%2) + b,
+      // and the 8 keys behind registers 8h .. 8h+7 are contiguous
+      // (kb*32 + 16h + 8g .. +8): the P^T operand of the next PV.
+#pragma unroll
+      for (int kb = 0; kb < BS / 32; ++kb) {
+        s[kb] = f32x16{};
+        const __bf16* ka = ks + (kb * 32 + krow0) * D;
+#pragma unroll
+        for (int m = 0; m < D / 16; ++m)
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              *reinterpret_cast<const bf16x8*>(ka + ((2 * m + g) ^ kswz) * 8), qf[m],
+              s[kb], 0, 0, 0);
+      }
+      pipeline_reads();
+    }
+  };
+
+  // VALU phase of tile i: start the copies of K(i+1) and V^T(i) (their
+  // buffers were last read in the MFMA phase just finished), then softmax(i).
+  auto valu_phase = [&](int32_t i) {
+    if (i < 0 || i >= n_grp) return;
+    const int32_t kt = tile_of(i);
+    if (i + 1 < n_grp) copy_k(tile_of(i + 1));
+    copy_v(kt);
+    const int32_t tcount = kt >= 0 ? tile_count[kt] : 0;
+    if (tcount != BS) {
+      // Keys of lane group g sit at bit 8g + (16(a/2) + 4(a%2) + b); a
+      // masked tile (kt < 0) has no valid key.
+#pragma unroll
+      for (int kb = 0; kb < BS / 32; ++kb) {
+        const uint32_t bits = (kt >= 0 ? tile_bits[kt * 4 + kb] : 0u) >> (8 * g);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int a = r / 4, b = r % 4;
+          if (!((bits >> (16 * (a / 2) + 4 * (a % 2) + b)) & 1u)) s[kb][r] = -INFINITY;
+        }
+      }
+    }
+    // Row max over the tile (raw dot products; the scale is positive).
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < BS / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    {
+      const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx),
+                                                       __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));   // max with lane ^ 32
+    }
+    // Lazy rescaling: the running max only moves (and O, l are rescaled)
+    // when some query's tile max exceeds it by more than 8 in log2 units;
+    // otherwise weights stay below 2^8 relative to the stale max, which
+    // fp32 accumulation and bf16 P absorb, and the final 1/l uses the same
+    // reference.  While no valid key has been seen the max stays -inf.
+    const float mt = mx * scale_log2;
+    if (__ballot(mt > m_run + 8.f) != 0) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+    }
+    const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+    float lsum = l_run;
+#pragma unroll
+    for (int kb = 0; kb < BS / 32; ++kb) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        f32x8 p;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          p[e] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * h + e], scale_log2, neg_m));
+        pb[kb][h] = __builtin_convertvector(p, bf16x8);
+        // Row sum of the bf16 weights the MFMA uses.
+        const bf16x8 w = pb[kb][h];
+        const bf16x2 one = {__bf16(1.f), __bf16(1.f)};
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 0, 1), one, lsum, false);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 2, 3), one, lsum, false);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 4, 5), one, lsum, false);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 6, 7), one, lsum, false);
+      }
+    }
+    l_run = lsum;
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);   // the copies have landed
+  };
+
+  if (n_grp > 0) copy_k(tile_of(0));
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __builtin_amdgcn_s_barrier();
+  // Phase pairs: group 0 runs MFMA(i) then VALU(i); group 1 runs VALU(i-1)
+  // then MFMA(i).  Both take the same number of barriers.  One loop per
+  // group, so that each loop carries either P or the scores, not both.
+  if (grp == 0) {
+    for (int32_t i = 0; i <= n_grp; ++i) {
+      mfma_phase(i);
+      __builtin_amdgcn_s_barrier();
+      valu_phase(i);
+      __builtin_amdgcn_s_barrier();
+    }
+  } else {
+    for (int32_t i = 0; i <= n_grp; ++i) {
+      valu_phase(i - 1);
+      __builtin_amdgcn_s_barrier();
+      mfma_phase(i);
+      __builtin_amdgcn_s_barrier();
+    }
+  }
+
+  // Merge: group 1 publishes O (register quads, lane-contiguous), m and l;
+  // group 0 combines them with its own and stores.
+  float4* ob = reinterpret_cast<float4*>(lds);
+  constexpr int kQuads = D / 32 * 4;
+  if (grp == 1) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        ob[((qw * kQuads + db * 4 + a) * 64) + lane] =
+            make_float4(o[db][4 * a], o[db][4 * a + 1], o[db][4 * a + 2], o[db][4 * a + 3]);
+    m_buf[qw * 64 + lane] = m_run;
+    l_buf[qw * 64 + lane] = l_run;
+  }
+  __syncthreads();
+  if (grp == 1) return;
+  const float m_b = m_buf[qw * 64 + lane], l_b = l_buf[qw * 64 + lane];
+  const float m_t = fmaxf(m_run, m_b);
+  const float fa = m_t == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_t);
+  const float fb = m_t == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_b - m_t);
+  const float l_own = l_run * fa + l_b * fb;
+  const float l_tot = l_own + __shfl_xor(l_own, 32);
+  const int qs = qw * 32 + li;
+  const bool qvalid = (tile_bits[qtile * 4 + qs / 32] >> (qs % 32)) & 1u;
+  const float inv = (qvalid && l_tot > 0.f) ? 1.f / l_tot : 0.f;
+  const float ca = fa * inv, cb = fb * inv;
+  // Lane (li, g) holds O^T[dd = db*32 + 8a + 4g + b][query li].
+  __bf16* dst = op + (bh * Lt + qrow) * D + 4 * g;
+  typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const float4 x = ob[((qw * kQuads + db * 4 + a) * 64) + lane];
+      const f32x4 f = {o[db][4 * a] * ca + x.x * cb, o[db][4 * a + 1] * ca + x.y * cb,
+                       o[db][4 * a + 2] * ca + x.z * cb, o[db][4 * a + 3] * ca + x.w * cb};
+      *reinterpret_cast<bf16x4*>(dst + db * 32 + 8 * a) = __builtin_convertvector(f, bf16x4);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- fp32
 
 template <int D, int BS>
@@ -451,6 +794,15 @@ void launch_bf16(const rf_plan* p, const void* qp, const void* kp,
                  const rf_keep& kc, float scale, hipStream_t st) {
   const int nb = p->sz.nb, n_tt = p->sz.n_text_tiles;
   dim3 grid(BH * (nb + n_tt));
+  if constexpr (BS == 128) {
+    hipLaunchKernelGGL((attn_bf16_pp_kernel<D>), grid, dim3(PpCfg<D>::kThreads), 0, st,
+                       static_cast<const __bf16*>(qp), static_cast<const __bf16*>(kp),
+                       static_cast<const __bf16*>(vt), kept, static_cast<__bf16*>(op),
+                       p->tile_bits, p->tile_count, p->sz.Lt, BH, nb, n_tt,
+                       kc.row_len_video, kc.nnz_per_head,
+                       scale * 1.4426950408889634f);
+    return;
+  }
   hipLaunchKernelGGL((attn_bf16_kernel<D, BS>), grid,
                      dim3(Bf16Cfg<D, BS>::kThreads), 0, st,
                      static_cast<const __bf16*>(qp), static_cast<const __bf16*>(kp),
