@@ -30,12 +30,8 @@ COMMON = [
 ]
 
 
-# Per-source extra flags.  The attention kernels pin their output
-# accumulators to AGPRs explicitly; every other MFMA result (the score tiles
-# the softmax reads) is kept in VGPRs.
-EXTRA = {
-    "attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-}
+# Per-source extra hipcc flags (none at present).
+EXTRA = {}
 
 
 def sources():
