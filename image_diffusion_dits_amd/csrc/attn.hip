@@ -638,6 +638,8 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
       }
     }
     l_run = lsum;
+    // The wait stays after the softmax, which it would otherwise precede.
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);   // the copies have landed
   };
 
