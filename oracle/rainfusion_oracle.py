@@ -39,6 +39,12 @@ each function restates the one it uses.
       query tiles attend to every tile.
   R8  Attention: o = sum_j softmax_j(q . k_j / sqrt(d)) v_j over the valid
       tokens of the row's kept tiles; pad query rows are 0.
+  R9  Attention recall (RF1 review, "What carries the argument": the masked
+      recall R' = S(Q', K', M') / S(Q', K', M_init), the attention mass that
+      survives a mask over the mass with no mask): for one query token,
+      R = sum of exp(q . k_j / sqrt(d)) over the valid tokens of its row's
+      kept tiles, divided by the same sum over every valid token of the
+      sequence.  Computed on chosen query tiles; pad query slots are NaN.
 """
 import math
 from dataclasses import dataclass
@@ -252,6 +258,38 @@ def sparse_attention(qp, kp, vp, kept, lay: Layout, scale=None,
                 s = (q @ k.T) * scale
                 p = np.exp(s - s.max(axis=1, keepdims=True))
                 out[b, h, qrows] = (p @ v) / p.sum(axis=1, keepdims=True)
+    return out
+
+
+def attention_recall(qp, kp, kept, lay: Layout, query_tiles, scale=None):
+    """Share of each query's dense softmax mass inside its kept tiles, fp64.
+
+    Reading R9 of the masked recall R' [RF1 review, "What carries the
+    argument"]: numerator over the valid keys of kept[b][h][i], denominator
+    over all valid keys.  qp, kp: [B, H, Np + n_text, d] in window order;
+    query_tiles: {(b, h): iterable of tile ids}.  Returns {(b, h, i): array
+    of bs recalls} with NaN at pad query slots."""
+    z = sizes(lay)
+    bs, Lp = z["bs"], z["Lp"]
+    d = qp.shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    valid = slot_valid(lay)
+    all_keys = np.flatnonzero(valid)
+    out = {}
+    for (b, h), tiles in query_tiles.items():
+        k_all = kp[b, h, all_keys].astype(np.float64)
+        for i in tiles:
+            r = np.full(bs, np.nan)
+            rows = np.arange(i * bs, min((i + 1) * bs, Lp))
+            rows = rows[valid[rows]]
+            kept_keys = np.concatenate([
+                np.arange(j * bs, min((j + 1) * bs, Lp)) for j in kept[b][h][i]])
+            in_kept = np.isin(all_keys, kept_keys)
+            if len(rows):
+                s = (qp[b, h, rows].astype(np.float64) @ k_all.T) * scale
+                e = np.exp(s - s.max(axis=1, keepdims=True))
+                r[rows - i * bs] = e[:, in_kept].sum(axis=1) / e.sum(axis=1)
+            out[(b, h, i)] = r
     return out
 
 

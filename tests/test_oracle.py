@@ -407,3 +407,115 @@ def test_query_tile_subset_marks_the_rest_nan():
     bs = z["bs"]
     assert np.array_equal(part[0, 0, 2 * bs:3 * bs], full[0, 0, 2 * bs:3 * bs])
     assert np.isnan(part[0, 0, :2 * bs]).all()
+
+
+# ---------------------------------------------------------------- recall R'
+
+def _recall_in_token_order(q, k, lay, kept, b=0, h=0):
+    """Independent path: dense softmax over the raster sequence, mass summed
+    over the tokens whose block is in the row's kept list."""
+    z = orc.sizes(lay)
+    blk = _token_block(lay, z)
+    s = q[b, h] @ k[b, h].T / math.sqrt(q.shape[-1])
+    p = scipy.special.softmax(s, axis=-1)
+    out = np.empty(z["L"])
+    for i in range(z["L"]):
+        mask = np.isin(blk, kept[b][h][blk[i]])
+        out[i] = p[i, mask].sum()
+    return out
+
+
+def _slots_to_tokens(rec, lay):
+    """{(b, h, tile): per-slot recall} -> per-token array for (0, 0)."""
+    z = orc.sizes(lay)
+    slot = orc.slot_of_token(lay)
+    text_slot = np.arange(z["Np"], z["Np"] + lay.n_text)
+    slots = np.concatenate([slot, text_slot])
+    bs = z["bs"]
+    return np.array([rec[(0, 0, s // bs)][s % bs] for s in slots])
+
+
+@pytest.mark.parametrize("permute,n_text", [(1, 0), (1, 5), (0, 3)])
+def test_recall_equals_dense_mass_in_token_order(permute, n_text):
+    lay = orc.Layout(3, 5, 7, 2, 2, 4, n_text=n_text, permute=permute)
+    z = orc.sizes(lay)
+    r = _rng(31)
+    q, k = (r.standard_normal((1, 1, z["L"], 8)) for _ in range(2))
+    nt = z["n_tiles"]
+    kept = [[[np.sort(r.choice(nt, size=r.integers(1, nt + 1), replace=False))
+              for _ in range(nt)]]]
+    rec = orc.attention_recall(orc.permute(q, lay), orc.permute(k, lay), kept, lay,
+                               {(0, 0): range(nt)})
+    np.testing.assert_allclose(_slots_to_tokens(rec, lay),
+                               _recall_in_token_order(q, k, lay, kept), atol=1e-12)
+    # Pad query slots are NaN, valid ones are in [0, 1].
+    valid = orc.slot_valid(lay)
+    bs = z["bs"]
+    for (b, h, i), v in rec.items():
+        vm = valid[i * bs:(i + 1) * bs]
+        vm = np.pad(vm, (0, bs - len(vm)))
+        assert np.isnan(v[~vm]).all() and ((v[vm] >= 0) & (v[vm] <= 1 + 1e-12)).all()
+
+
+def test_recall_zero_sparsity_is_one():
+    lay = orc.Layout(3, 16, 16, 1, 8, 8, sink=1)
+    z = orc.sizes(lay)
+    r = _rng(37)
+    q, k, v = (r.standard_normal((1, 1, z["L"], 8)) for _ in range(3))
+    res = orc.run(q, k, v, lay, 0)
+    rec = orc.attention_recall(res["qp"], res["kp"], res["kept"], lay,
+                               {(0, 0): range(z["n_tiles"])})
+    vals = np.concatenate(list(rec.values()))
+    np.testing.assert_allclose(vals[~np.isnan(vals)], 1.0, atol=1e-15)
+
+
+def test_recall_with_uniform_logits_is_the_kept_key_share():
+    """k = 0 makes every logit 0: the recall is the number of valid kept
+    keys over the number of valid keys (closed form)."""
+    lay = orc.Layout(2, 6, 6, 1, 4, 4, n_text=3)
+    z = orc.sizes(lay)
+    r = _rng(41)
+    q = orc.permute(r.standard_normal((1, 1, z["L"], 4)), lay)
+    kz = np.zeros_like(q)
+    nt = z["n_tiles"]
+    kept = [[[np.sort(r.choice(nt, size=r.integers(1, nt + 1), replace=False))
+              for _ in range(nt)]]]
+    rec = orc.attention_recall(q, kz, kept, lay, {(0, 0): range(nt)})
+    counts = np.concatenate([orc.block_counts(lay),
+                             [min(z["bs"], lay.n_text - j * z["bs"])
+                              for j in range(z["n_text_tiles"])]])
+    for i in range(nt):
+        want = counts[kept[0][0][i]].sum() / z["L"]
+        v = rec[(0, 0, i)]
+        np.testing.assert_allclose(v[~np.isnan(v)], want, atol=1e-15)
+
+
+def test_recall_of_complementary_masks_sums_to_one():
+    lay = orc.Layout(2, 8, 8, 1, 4, 4)
+    z = orc.sizes(lay)
+    r = _rng(43)
+    q, k = (orc.permute(r.standard_normal((1, 1, z["L"], 4)), lay) for _ in range(2))
+    nt = z["n_tiles"]
+    a = [np.sort(r.choice(nt, size=3, replace=False)) for _ in range(nt)]
+    c = [np.setdiff1d(np.arange(nt), x) for x in a]
+    ra = orc.attention_recall(q, k, [[a]], lay, {(0, 0): range(nt)})
+    rc = orc.attention_recall(q, k, [[c]], lay, {(0, 0): range(nt)})
+    for key in ra:
+        np.testing.assert_allclose(ra[key] + rc[key], 1.0, atol=1e-13)
+
+
+def test_recall_follows_a_planted_dominant_key():
+    """One key equal to a large multiple of query 0 holds almost all of that
+    query's mass: recall is ~1 when its tile is kept and ~0 when not."""
+    lay = orc.Layout(2, 8, 8, 1, 4, 4)
+    z = orc.sizes(lay)
+    r = _rng(47)
+    qp = orc.permute(0.1 * r.standard_normal((1, 1, z["L"], 4)), lay)
+    kp = orc.permute(0.1 * r.standard_normal((1, 1, z["L"], 4)), lay)
+    qp[0, 0, 0] = [1.0, 0.0, 0.0, 0.0]
+    kp[0, 0, 3 * z["bs"] + 1] = [200.0, 0.0, 0.0, 0.0]   # slot in tile 3
+    nt = z["n_tiles"]
+    with_t3 = [[[np.array([0, 3])] + [np.arange(nt)] * (nt - 1)]]
+    without = [[[np.array([0, 1])] + [np.arange(nt)] * (nt - 1)]]
+    assert orc.attention_recall(qp, kp, with_t3, lay, {(0, 0): [0]})[(0, 0, 0)][0] > 1 - 1e-12
+    assert orc.attention_recall(qp, kp, without, lay, {(0, 0): [0]})[(0, 0, 0)][0] < 1e-12
