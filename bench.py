@@ -50,7 +50,57 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, run a plain elementwise copy of "
                          "known size (counter calibration)")
+    ap.add_argument("--recall", type=int, default=0, metavar="N",
+                    help="instead of the step benchmark, measure the attention "
+                         "recall of N sampled query tiles per head at each "
+                         "sweep sparsity, permutation on and off")
     return ap.parse_args()
+
+
+def recall_study(n_sample):
+    """Mean share of each sampled query's dense softmax mass inside its kept
+    tiles (the masked recall R'), 720p tensors, permutation on vs off, at the
+    sweep sparsities; prints one JSON line."""
+    import numpy as np
+    import torch
+
+    from image_diffusion_dits_amd import configs, inputs, rf
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    out = {"metric": "attention recall (share of dense softmax mass in kept tiles)",
+           "unit": "fraction", "higher_is_better": True, "data": "synthetic",
+           "samples_per_head": n_sample, "modes": {}}
+    for cfg in (configs.SWEEP, configs.SWEEP_RASTER):
+        q, k, _ = inputs.make_qkv(cfg, dev)
+        plan = rf.Plan(cfg.layout)
+        qp, qbar = rf.permute_means(plan, q)
+        kp, kbar = rf.permute_means(plan, k)
+        z = plan.sizes
+        rng = np.random.default_rng(7)
+        tiles = np.sort(rng.choice(z["nb"], size=min(n_sample, z["nb"]), replace=False))
+        st = torch.tensor(tiles, dtype=torch.int32, device=dev)
+        mode = {}
+        for s in cfg.sparsity:
+            kept = rf.predict_mask(plan, qbar, kbar, s)
+            rec = rf.attention_recall(plan, qp, kp, kept, s, st)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            rf.attention_recall(plan, qp, kp, kept, s, st, out=rec)
+            e1.record()
+            torch.cuda.synchronize()
+            r = rec.cpu().numpy()
+            mode[str(s)] = {"kept_tiles_per_row": plan.keep(s)["k_eff"],
+                            "mean": round(float(np.nanmean(r)), 5),
+                            "p10": round(float(np.nanpercentile(r, 10)), 5),
+                            "min": round(float(np.nanmin(r)), 5),
+                            "ms": round(e0.elapsed_time(e1), 3)}
+            print(f"[recall] {cfg.name} s={s}: {mode[str(s)]}", file=sys.stderr, flush=True)
+        out["modes"][cfg.name] = mode
+        plan.close()
+        del q, k, qp, kp
+    print(json.dumps(out))
+    return 0
 
 
 def source_hash(path):
@@ -120,6 +170,8 @@ def cpu_baseline(cfg, q, k, v, sparsity, n_tiles_sample, exec_flop_total):
 
 def main():
     a = parse()
+    if a.recall:
+        return recall_study(a.recall)
     if a.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported "
               "(every step is independent per head; the multi-GPU layout is "

@@ -69,6 +69,8 @@ _SIGNATURES = {
                         _vp, _vp],
     "rf_sparse_attn": [_vp, _vp, _vp, _vp, _vp, _c_i32, _vp, _c_i32, _c_i32,
                        _c_i32, _c_f32, ctypes.c_int, _vp],
+    "rf_attention_recall": [_vp, _vp, _vp, _vp, _c_i32, _vp, _c_i32, _c_i32,
+                            _c_i32, _c_i32, _c_f32, ctypes.c_int, _vp, _vp],
 }
 
 _lib = None
@@ -287,6 +289,27 @@ def sparse_attn(plan, qp, kp, vt, kept, sparsity_pct, scale=None, out=None):
                                 _ptr(kept), int(sparsity_pct), _ptr(out), B, H,
                                 d, float(scale), _dtype_code(qp), _stream()),
            "rf_sparse_attn")
+    return out
+
+
+def attention_recall(plan, qp, kp, kept, sparsity_pct, sample_tiles, scale=None,
+                     out=None):
+    """Share of each sampled query's dense softmax mass inside its kept tiles.
+
+    sample_tiles: int32 tensor of query-tile ids on the device.  Returns fp32
+    [B, H, n_sample, bs] (NaN at pad query slots)."""
+    B, H, d = _bhd(qp)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    n = sample_tiles.numel()
+    if out is None:
+        out = torch.empty((B, H, n, plan.sizes["bs"]), dtype=torch.float32,
+                          device=qp.device)
+    _check(lib().rf_attention_recall(plan.handle, _ptr(qp), _ptr(kp), _ptr(kept),
+                                     int(sparsity_pct), _ptr(sample_tiles), n, B, H,
+                                     d, float(scale), _dtype_code(qp), _ptr(out),
+                                     _stream()),
+           "rf_attention_recall")
     return out
 
 

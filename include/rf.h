@@ -209,6 +209,27 @@ rf_status rf_sparse_attn(const rf_plan* plan, const void* qp, const void* kp,
                          int32_t d, float scale, rf_dtype dtype,
                          hipStream_t stream);
 
+/* Attention-recall diagnostic [RF1 review, "What carries the argument":
+ * the masked recall R', attention mass that survives a mask over the mass
+ * with no mask].  For each sampled query tile t = sample_tiles[s] and each
+ * valid query slot of it: recall = the sum of exp(scale * q . k_j) over the
+ * valid slots j of the tiles listed in row t of kept_idx, divided by the
+ * same sum over every valid slot of the sequence (the dense softmax
+ * denominator).  fp32 arithmetic with a running maximum (bf16 or fp32
+ * operands); cost is dense attention logits for the sampled tiles only.
+ * qp, kp: [B][H][Lt][d] RF_ROWS; kept_idx as for rf_sparse_attn (entries
+ * out of range are ignored); sample_tiles: device int32 [n_sample], an id
+ * outside [0, n_tiles) yields NaN for the whole sample; recall: fp32
+ * [B][H][n_sample][bs], NaN at pad query slots.  n_sample >= 1,
+ * n_tiles <= 262144, d in {64, 128}. */
+rf_status rf_attention_recall(const rf_plan* plan, const void* qp,
+                              const void* kp, const int32_t* kept_idx,
+                              int32_t sparsity_pct,
+                              const int32_t* sample_tiles, int32_t n_sample,
+                              int32_t B, int32_t H, int32_t d, float scale,
+                              rf_dtype dtype, float* recall,
+                              hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

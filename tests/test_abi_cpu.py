@@ -132,6 +132,8 @@ def test_gpu_entry_points_reject_bad_arguments_without_a_device():
     assert L.rf_predict_mask(None, buf, buf, 1, 1, 64, 50, buf, None, None) == rf.ERR_INVALID_ARG
     assert L.rf_sparse_attn(None, buf, buf, buf, buf, 50, buf, 1, 1, 64, 0.125,
                             rf.BF16, None) == rf.ERR_INVALID_ARG
+    assert L.rf_attention_recall(None, buf, buf, buf, 50, buf, 1, 1, 1, 64, 0.125,
+                                 rf.BF16, buf, None) == rf.ERR_INVALID_ARG
     assert b"null plan" in L.rf_last_error()
     assert L.rf_plan_sizes(None, None) == rf.ERR_INVALID_ARG
     L.rf_plan_destroy(None)  # no-op

@@ -1,0 +1,135 @@
+"""Parity of the attention-recall diagnostic (through the C-ABI) with the fp64
+oracle: the share of each sampled query's dense softmax mass inside its kept
+tiles, on the kept lists the GPU predicted and the permuted tensors it made.
+
+Tolerance: both sides see the same operand values; the GPU accumulates the
+two exponential sums in fp32 with a running maximum, the oracle in fp64, so
+the recall may differ by a few fp32 roundings per term of the sum: 2e-5
+absolute up to 10k keys, 1e-4 beyond.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import parity
+from image_diffusion_dits_amd import configs, inputs, rf
+from oracle import rainfusion_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _tol(n_keys):
+    return 2e-5 if n_keys <= 10000 else 1e-4
+
+
+def check_recall(lay_dict, q, k, s, heads=None, samples=None, seed=0):
+    """GPU recall on `samples` query tiles (default: first, last, and two
+    random ones) of `heads` (default: all) against the oracle."""
+    lay = parity.olayout(lay_dict)
+    z = orc.sizes(lay)
+    plan = rf.Plan(lay_dict)
+    qp, qbar = rf.permute_means(plan, q)
+    kp, kbar = rf.permute_means(plan, k)
+    kept = rf.predict_mask(plan, qbar, kbar, s)
+    nt = z["n_tiles"]
+    if samples is None:
+        rng = np.random.default_rng(seed)
+        samples = sorted({0, nt - 1, *rng.integers(0, nt, size=2).tolist()})
+    st = torch.tensor(samples, dtype=torch.int32, device="cuda")
+    rec = rf.attention_recall(plan, qp, kp, kept, s, st)
+    torch.cuda.synchronize()
+    got = rec.cpu().numpy()
+    rows = rf.kept_rows(plan, kept, s)
+    B, H = q.shape[:2]
+    Lp = z["Lp"]
+    worst = 0.0
+    tol = _tol(int(orc.slot_valid(lay).sum()))
+    for b in range(B):
+        for h in (range(H) if heads is None else heads):
+            qv = parity.values(qp[b:b + 1, h:h + 1, :Lp])
+            kv = parity.values(kp[b:b + 1, h:h + 1, :Lp])
+            want = orc.attention_recall(qv, kv, [[rows[b][h]]], lay,
+                                        {(0, 0): samples})
+            for si, t in enumerate(samples):
+                w, g = want[(0, 0, t)], got[b, h, si]
+                assert np.array_equal(np.isnan(w), np.isnan(g)), f"pad slots b{b} h{h} t{t}"
+                m = ~np.isnan(w)
+                err = np.abs(g[m] - w[m]).max() if m.any() else 0.0
+                worst = max(worst, err)
+                assert err <= tol, f"recall b{b} h{h} tile {t}: {err:.3e} > {tol:.0e}"
+    say(f"  recall max_abs={worst:.3e} (tol {tol:.0e}) over samples {samples}")
+    plan.close()
+    return got
+
+
+def _iid(shape, seed, dtype):
+    return inputs.random_tensor(shape, seed, device="cuda", dtype=dtype)
+
+
+EDGE = [
+    ("ragged3d-text77", dict(T=3, H=13, W=21, wt=2, wh=8, ww=8, n_text=77,
+                             permute=1, sink=1), 2, 3, 128, torch.bfloat16, 70),
+    ("bs64-d64", dict(T=2, H=10, W=9, wt=1, wh=8, ww=8, n_text=0, permute=1,
+                      sink=1), 1, 2, 64, torch.bfloat16, 50),
+    ("raster-bs64-text10", dict(T=3, H=7, W=11, wt=1, wh=8, ww=8, n_text=10,
+                                permute=0, sink=1), 1, 2, 128, torch.bfloat16, 60),
+    ("f32-d64-bs64-raster", dict(T=2, H=5, W=30, wt=1, wh=8, ww=8, n_text=64,
+                                 permute=0, sink=1), 1, 2, 64, torch.float32, 75),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
+def test_recall_edge_layouts(case):
+    name, lay, B, H, d, dt, s = case
+    say(f"[recall edge] {name} B={B} H={H} d={d} {dt} s={s}")
+    L = rf.layout_sizes(lay)["L"]
+    nt = rf.layout_sizes(lay)["n_tiles"]
+    q, k = _iid((B, H, L, d), 21, dt), _iid((B, H, L, d), 22, dt)
+    check_recall(lay, q, k, s, samples=list(range(nt)))
+
+
+def test_recall_tiny_and_image_workloads():
+    for cfg in (configs.TINY, configs.IMAGE):
+        say(f"[recall workload] {cfg.name}")
+        q, k, _ = inputs.make_qkv(cfg, "cuda")
+        check_recall(cfg.layout, q, k, cfg.sparsity[0])
+
+
+def test_recall_video720_workload():
+    cfg = configs.VIDEO720
+    say(f"[recall workload] {cfg.name} (4 heads)")
+    q, k, _ = inputs.make_qkv(cfg, "cuda", H=4)
+    check_recall(cfg.layout, q, k, cfg.sparsity[0])
+
+
+def test_recall_long_text_workload():
+    cfg = configs.VIDEO_LONG
+    z = rf.layout_sizes(cfg.layout)
+    say(f"[recall workload] {cfg.name} (2 heads, text query tiles included)")
+    q, k, _ = inputs.make_qkv(cfg, "cuda", H=2)
+    check_recall(cfg.layout, q, k, cfg.sparsity[0],
+                 samples=[0, 7, z["nb"] - 1, z["nb"], z["n_tiles"] - 1])
+
+
+def test_recall_is_one_without_sparsity_and_nan_for_bad_samples():
+    lay = dict(T=3, H=13, W=21, wt=2, wh=8, ww=8, n_text=77, permute=1, sink=1)
+    say("[recall] s = 0 and out-of-range sample ids")
+    z = rf.layout_sizes(lay)
+    q, k = _iid((1, 2, z["L"], 128), 31, torch.bfloat16), _iid((1, 2, z["L"], 128), 32, torch.bfloat16)
+    plan = rf.Plan(lay)
+    qp, qbar = rf.permute_means(plan, q)
+    kp, kbar = rf.permute_means(plan, k)
+    kept = rf.predict_mask(plan, qbar, kbar, 0)
+    st = torch.tensor([0, -1, z["n_tiles"], z["n_tiles"] - 1], dtype=torch.int32, device="cuda")
+    rec = rf.attention_recall(plan, qp, kp, kept, 0, st).cpu().numpy()
+    for si in (0, 3):
+        v = rec[:, :, si]
+        np.testing.assert_allclose(v[~np.isnan(v)], 1.0, atol=1e-6)
+    assert np.isnan(rec[:, :, 1]).all() and np.isnan(rec[:, :, 2]).all()
+    plan.close()
