@@ -54,7 +54,58 @@ def parse():
                     help="instead of the step benchmark, measure the attention "
                          "recall of N sampled query tiles per head at each "
                          "sweep sparsity, permutation on and off")
+    ap.add_argument("--schedule", type=int, default=0, metavar="N",
+                    help="instead of the step benchmark, time an N-step sampling "
+                         "run of one attention layer under the timestep policy "
+                         "(first 10%% of steps dense) on the 720p workload")
+    ap.add_argument("--refresh", type=int, default=1,
+                    help="with --schedule: predict the mask every R sparse steps")
     return ap.parse_args()
+
+
+def schedule_study(n_steps, refresh, sparsity):
+    """Attention time per step over a sampling run under the timestep policy,
+    against an all-dense run; prints one JSON line."""
+    import numpy as np
+    import torch
+
+    from image_diffusion_dits_amd import configs, inputs
+    from image_diffusion_dits_amd.policy import SparseAttention, StepPolicy
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    cfg = configs.VIDEO720
+    q, k, v = inputs.make_qkv(cfg, dev)
+    pol = StepPolicy(n_steps, dense_fraction=0.10, sparsity_pct=sparsity,
+                     refresh_every=refresh)
+    layer = SparseAttention(cfg.layout, pol, cfg.B, cfg.H, cfg.d, q.dtype, dev)
+    out = torch.empty_like(q)
+    for t in sorted({0, pol.n_dense}):         # warm both kinds of step
+        if t < n_steps:
+            layer(q, k, v, t, out=out)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_steps + 1)]
+    ev[0].record()
+    for t in range(n_steps):
+        layer(q, k, v, t, out=out)
+        ev[t + 1].record()
+    torch.cuda.synchronize()
+    ms = [ev[t].elapsed_time(ev[t + 1]) for t in range(n_steps)]
+    modes = pol.schedule()
+    by = {m: [x for x, mm in zip(ms, modes) if mm == m] for m in set(modes)}
+    dense = float(np.median(by["dense"])) if "dense" in by else None
+    mean = float(np.mean(ms))
+    layer.close()
+    print(json.dumps({
+        "metric": "attention ms per sampling step under the timestep policy",
+        "unit": "ms", "higher_is_better": False, "data": "synthetic",
+        "config": {"workload": cfg.name, "steps": n_steps, "dense_fraction": 0.10,
+                   "sparsity_pct": sparsity, "refresh_every": refresh},
+        "mean_ms_per_step": round(mean, 3),
+        "ms_by_mode": {m: round(float(np.median(x)), 3) for m, x in by.items()},
+        "steps_by_mode": {m: len(x) for m, x in by.items()},
+        "speedup_vs_all_dense": round(dense / mean, 3) if dense else None}))
+    return 0
 
 
 def recall_study(n_sample):
@@ -172,6 +223,9 @@ def main():
     a = parse()
     if a.recall:
         return recall_study(a.recall)
+    if a.schedule:
+        return schedule_study(a.schedule, a.refresh,
+                              a.sparsity if a.sparsity is not None else 80)
     if a.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported "
               "(every step is independent per head; the multi-GPU layout is "
