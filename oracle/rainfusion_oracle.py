@@ -45,6 +45,29 @@ each function restates the one it uses.
       R = sum of exp(q . k_j / sqrt(d)) over the valid tokens of its row's
       kept tiles, divided by the same sum over every valid token of the
       sequence.  Computed on chosen query tiles; pad query slots are NaN.
+  R10 v1 head patterns as tile masks (RF1 review, "What carries the
+      argument", "Core claim" and the free-parameter list: striped bands for
+      spatial and temporal heads, bandwidth 1/4 giving a 9/16 cut; the
+      checkerboard C = {a_ij : i mod tau = k and j mod tau = k}, tau = 2).
+      Tiles play the role of tokens.  Band half-width w = floor(b nb + 1/2)
+      video tiles for bandwidth b, so the kept area of the band on the unit
+      square is 1 - (1 - b)^2 (7/16 at b = 1/4).  Spatial: video query tile i
+      keeps video tile j when |i - j| <= w, tiles in frame-major order (the
+      block index).  Temporal: |r(i) - r(j)| <= w with r the rank of a tile
+      in spatial-major order, i.e. tiles sorted by (h, w, t) of their first
+      valid token.  Textural: j = i (mod tau).  Text tiles are appended to
+      every video row and text query rows keep every tile (R7).
+  R11 ARM, the v1 online classifier (RF1 review, "What carries the argument"
+      and "Core claim"): the local sample is every omega_l-th raster token of
+      frame 0, the global sample every omega_g-th raster token of the video;
+      queries and keys are the same sampled tokens.  Per sampled query the
+      recall is R' of R9 restricted to the sampled keys, with the candidate
+      mask evaluated on the tiles that hold the two tokens: the temporal mask
+      on the local sample (bR), the spatial mask on the global sample (eR).
+      A head's recall is the mean over its sample.  Class: temporal if
+      bR >= alpha, else spatial if eR >= alpha, else textural.  The pages give
+      neither alpha nor omega; alpha = 0.9 follows the 90% recall target of
+      the v1 page's RainFusion+ variant, and the strides are parameters.
 """
 import math
 from dataclasses import dataclass
@@ -291,6 +314,113 @@ def attention_recall(qp, kp, kept, lay: Layout, query_tiles, scale=None):
                 r[rows - i * bs] = e[:, in_kept].sum(axis=1) / e.sum(axis=1)
             out[(b, h, i)] = r
     return out
+
+
+SPATIAL, TEMPORAL, TEXTURAL = 0, 1, 2
+
+
+def band_halfwidth(lay: Layout, bandwidth: float) -> int:
+    """w = floor(b nb + 1/2) video tiles, reading R10."""
+    return int(math.floor(bandwidth * sizes(lay)["nb"] + 0.5))
+
+
+def tile_rank(lay: Layout) -> np.ndarray:
+    """r(i): position of video tile i when the tiles are sorted by (h, w, t)
+    of their first valid token (spatial-major order), reading R10."""
+    z = sizes(lay)
+    src = np.full(z["Np"], -1, dtype=np.int64)
+    src[slot_of_token(lay)] = np.arange(z["N"])
+    first = []
+    for i in range(z["nb"]):
+        toks = src[i * z["bs"]:(i + 1) * z["bs"]]
+        first.append(toks[toks >= 0][0])
+    first = np.array(first)
+    t, rem = np.divmod(first, lay.H * lay.W)
+    h, w = np.divmod(rem, lay.W)
+    order = np.lexsort((t, w, h))          # last key is the primary one
+    rank = np.empty(z["nb"], dtype=np.int64)
+    rank[order] = np.arange(z["nb"])
+    return rank
+
+
+def pattern_keeps(lay: Layout, pattern: int, w: int, tau: int) -> np.ndarray:
+    """Boolean [nb, nb] video-tile mask of one v1 head pattern, reading R10.
+    [RF1 review, "What carries the argument"; free parameters bandwidth and
+    tau]."""
+    nb = sizes(lay)["nb"]
+    i = np.arange(nb)[:, None]
+    j = np.arange(nb)[None, :]
+    if pattern == SPATIAL:
+        return np.abs(i - j) <= w
+    if pattern == TEMPORAL:
+        r = tile_rank(lay)
+        return np.abs(r[:, None] - r[None, :]) <= w
+    if pattern == TEXTURAL:
+        # the union over k of {i mod tau = k and j mod tau = k}
+        return np.logical_or.reduce([(i % tau == k) & (j % tau == k)
+                                     for k in range(tau)])
+    raise ValueError(f"pattern {pattern}")
+
+
+def pattern_mask(lay: Layout, head_pattern, w: int, tau: int):
+    """Kept tiles per query tile for every (b, h), in the list-of-rows form
+    of `predict_mask`: video rows from `pattern_keeps` of the head's pattern
+    plus the text tiles, text rows every tile (R7, R10).
+    head_pattern: int array [B, H]."""
+    z = sizes(lay)
+    nb, n_tiles = z["nb"], z["n_tiles"]
+    text_tiles = np.arange(nb, n_tiles)
+    masks = {}
+    kept = []
+    hp = np.asarray(head_pattern)
+    for b in range(hp.shape[0]):
+        per_head = []
+        for h in range(hp.shape[1]):
+            p = int(hp[b, h])
+            if p not in masks:
+                masks[p] = pattern_keeps(lay, p, w, tau)
+            rows = [np.concatenate([np.flatnonzero(masks[p][i]), text_tiles])
+                    for i in range(nb)]
+            rows += [np.arange(n_tiles) for _ in range(z["n_text_tiles"])]
+            per_head.append(rows)
+        kept.append(per_head)
+    return kept
+
+
+def arm_samples(lay: Layout, local: bool, stride: int) -> np.ndarray:
+    """Raster ids of ARM's sampled tokens, reading R11: every stride-th token
+    of frame 0 (local) or of the whole video (global)."""
+    limit = lay.H * lay.W if local else lay.T * lay.H * lay.W
+    return np.arange(0, limit, stride, dtype=np.int64)
+
+
+def arm_recall(q, k, lay: Layout, pattern: int, w: int, tau: int, tokens,
+               scale=None) -> np.ndarray:
+    """Per sampled query, the share of its softmax mass over the sampled keys
+    that falls on keys its tile keeps under `pattern`, fp64.  Reading R11 of
+    R' = S(Q', K', M') / S(Q', K', M_init) [RF1 review, "What carries the
+    argument"].  q, k: raster [B, H, N + n_text, d].  Returns [B, H, n]."""
+    z = sizes(lay)
+    d = q.shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    tokens = np.asarray(tokens)
+    tile = slot_of_token(lay)[tokens] // z["bs"]
+    m = pattern_keeps(lay, pattern, w, tau)[tile[:, None], tile[None, :]]
+    qs = q[:, :, tokens].astype(np.float64)
+    ks = k[:, :, tokens].astype(np.float64)
+    s = np.matmul(qs, np.swapaxes(ks, -1, -2)) * scale
+    e = np.exp(s - s.max(axis=-1, keepdims=True))
+    return (e * m).sum(axis=-1) / e.sum(axis=-1)
+
+
+def arm_classify(local_recall, global_recall, alpha: float) -> np.ndarray:
+    """Head pattern from the per-sample recalls [B, H, n], reading R11:
+    temporal if mean local >= alpha, else spatial if mean global >= alpha,
+    else textural.  [RF1 review, "Core claim", classification order]."""
+    bR = np.mean(local_recall, axis=-1)
+    eR = np.mean(global_recall, axis=-1)
+    return np.where(bR >= alpha, TEMPORAL,
+                    np.where(eR >= alpha, SPATIAL, TEXTURAL))
 
 
 def run(q, k, v, lay: Layout, sparsity_pct: int, query_tiles=None):

@@ -519,3 +519,197 @@ def test_recall_follows_a_planted_dominant_key():
     without = [[[np.array([0, 1])] + [np.arange(nt)] * (nt - 1)]]
     assert orc.attention_recall(qp, kp, with_t3, lay, {(0, 0): [0]})[(0, 0, 0)][0] > 1 - 1e-12
     assert orc.attention_recall(qp, kp, without, lay, {(0, 0): [0]})[(0, 0, 0)][0] < 1e-12
+
+
+# ------------------------------------------------------- v1 head patterns
+
+def _first_token_coords(lay, z):
+    """(t, h, w) of the first valid token of each video tile, by walking the
+    grid token by token (brute force, no slot arithmetic)."""
+    first = {}
+    for t in range(lay.T):
+        for h in range(lay.H):
+            for w in range(lay.W):
+                n = (t * lay.H + h) * lay.W + w
+                if lay.permute:
+                    blk = (((t // lay.wt) * z["nH"] + h // lay.wh) * z["nW"]
+                           + w // lay.ww)
+                    inner = ((t % lay.wt) * lay.wh + h % lay.wh) * lay.ww + w % lay.ww
+                else:
+                    blk, inner = divmod(n, z["bs"])
+                if blk not in first or inner < first[blk][0]:
+                    first[blk] = (inner, (t, h, w))
+    return [first[i][1] for i in range(z["nb"])]
+
+
+def test_tile_rank_in_window_order_is_bh_bw_bt():
+    """With the window order, sorting tiles by (h, w, t) of their first token
+    is sorting by block coordinates (bh, bw, bt): r = (bh nW + bw) nT + bt."""
+    lay = orc.Layout(5, 7, 9, 2, 2, 4)
+    z = orc.sizes(lay)
+    r = orc.tile_rank(lay)
+    for i in range(z["nb"]):
+        bt, rem = divmod(i, z["nH"] * z["nW"])
+        bh, bw = divmod(rem, z["nW"])
+        assert r[i] == (bh * z["nW"] + bw) * z["nT"] + bt
+
+
+@pytest.mark.parametrize("dims,permute", [((3, 5, 7, 2, 2, 4), 0),
+                                          ((4, 6, 10, 1, 2, 8), 0),
+                                          ((3, 5, 7, 2, 2, 4), 1)])
+def test_tile_rank_sorts_first_tokens_spatial_major(dims, permute):
+    lay = orc.Layout(*dims, permute=permute)
+    z = orc.sizes(lay)
+    coords = _first_token_coords(lay, z)
+    r = orc.tile_rank(lay)
+    assert sorted(r.tolist()) == list(range(z["nb"]))
+    for i, j in itertools.combinations(range(z["nb"]), 2):
+        (ti, hi, wi), (tj, hj, wj) = coords[i], coords[j]
+        assert (r[i] < r[j]) == ((hi, wi, ti) < (hj, wj, tj))
+
+
+def test_band_kept_count_closed_form():
+    """A band |i - j| <= w on n x n keeps n (2w + 1) - w (w + 1) entries;
+    the temporal band is the same band in another order, so it keeps as
+    many."""
+    lay = orc.Layout(5, 7, 9, 2, 2, 4)
+    n = orc.sizes(lay)["nb"]
+    for w in (0, 1, 5, n // 4, n - 2):
+        want = n * (2 * w + 1) - w * (w + 1)
+        for p in (orc.SPATIAL, orc.TEMPORAL):
+            assert orc.pattern_keeps(lay, p, w, 2).sum() == want
+
+
+def test_bandwidth_quarter_cuts_nine_sixteenths():
+    """Bandwidth 1/4 keeps 1 - (3/4)^2 = 7/16 of the tile pairs, the 9/16
+    reduction the v1 page states, up to O(1/nb)."""
+    lay = orc.Layout(21, 45, 80, 2, 8, 8)
+    n = orc.sizes(lay)["nb"]
+    assert n == 660
+    w = orc.band_halfwidth(lay, 0.25)
+    assert w == 165
+    for p in (orc.SPATIAL, orc.TEMPORAL):
+        frac = orc.pattern_keeps(lay, p, w, 2).mean()
+        assert abs(frac - 7 / 16) < 1.0 / n
+
+
+def test_temporal_equals_spatial_with_one_frame_window():
+    """With a single window along time the spatial-major order of the tiles
+    is the block order itself, so the two bands coincide."""
+    lay = orc.Layout(1, 16, 24, 1, 4, 8)
+    for w in (0, 3, 7):
+        np.testing.assert_array_equal(orc.pattern_keeps(lay, orc.TEMPORAL, w, 2),
+                                      orc.pattern_keeps(lay, orc.SPATIAL, w, 2))
+
+
+@pytest.mark.parametrize("tau", [1, 2, 3, 4])
+def test_textural_checkerboard_keeps_one_residue_class(tau):
+    """The union over k of {i = k and j = k (mod tau)} is j = i (mod tau):
+    row i keeps ceil((nb - i mod tau) / tau) tiles."""
+    lay = orc.Layout(5, 7, 9, 2, 2, 4)
+    n = orc.sizes(lay)["nb"]
+    m = orc.pattern_keeps(lay, orc.TEXTURAL, 0, tau)
+    for i in range(n):
+        assert np.flatnonzero(m[i]).tolist() == list(range(i % tau, n, tau))
+    assert m.sum(axis=1).tolist() == [-(-(n - i % tau) // tau) for i in range(n)]
+
+
+def test_pattern_masks_are_symmetric_and_keep_the_diagonal():
+    lay = orc.Layout(3, 5, 7, 2, 2, 4, permute=0)
+    for p, w, tau in [(orc.SPATIAL, 2, 2), (orc.TEMPORAL, 2, 2), (orc.TEXTURAL, 0, 3)]:
+        m = orc.pattern_keeps(lay, p, w, tau)
+        np.testing.assert_array_equal(m, m.T)
+        assert m.diagonal().all()
+
+
+def test_pattern_rows_with_text_and_full_band_is_dense_attention():
+    """A band wider than the grid keeps every tile, so the attention equals
+    textbook dense attention."""
+    lay = orc.Layout(2, 6, 6, 1, 4, 4, n_text=5)
+    z = orc.sizes(lay)
+    hp = np.array([[orc.SPATIAL, orc.TEMPORAL]])
+    kept = orc.pattern_mask(lay, hp, z["nb"], 2)
+    for rows in kept[0]:
+        assert len(rows) == z["n_tiles"]
+        for row in rows:
+            assert row.tolist() == list(range(z["n_tiles"]))
+    r = _rng(53)
+    q, k, v = (r.standard_normal((1, 2, z["L"], 8)) for _ in range(3))
+    qp, kp, vp = (orc.permute(x, lay) for x in (q, k, v))
+    o = orc.unpermute(orc.sparse_attention(qp, kp, vp, kept, lay), lay)
+    np.testing.assert_allclose(o, _dense_attention(q, k, v), atol=1e-12)
+
+
+def test_pattern_rows_append_text_tiles():
+    lay = orc.Layout(3, 5, 7, 2, 2, 4, n_text=9)
+    z = orc.sizes(lay)
+    nb, nt = z["nb"], z["n_tiles"]
+    kept = orc.pattern_mask(lay, np.array([[orc.TEXTURAL]]), 0, 2)[0][0]
+    assert len(kept) == nt
+    for i in range(nb):
+        assert kept[i].tolist() == list(range(i % 2, nb, 2)) + list(range(nb, nt))
+    for i in range(nb, nt):
+        assert kept[i].tolist() == list(range(nt))
+
+
+# ------------------------------------------------------------------ ARM
+
+def test_arm_samples():
+    lay = orc.Layout(3, 5, 7, 2, 2, 4)
+    assert orc.arm_samples(lay, True, 4).tolist() == [0, 4, 8, 12, 16, 20, 24, 28, 32]
+    g = orc.arm_samples(lay, False, 8)
+    assert len(g) == -(-105 // 8) and g[-1] == 104
+
+
+def test_arm_recall_two_tokens_is_a_sigmoid():
+    """Two sampled tokens in different tiles, a mask that keeps only the
+    query's own tile: R' = e^{s_aa} / (e^{s_aa} + e^{s_ab})."""
+    lay = orc.Layout(1, 8, 8, 1, 4, 4)
+    r = _rng(59)
+    q, k = (r.standard_normal((1, 1, 64, 4)) for _ in range(2))
+    toks = np.array([0, 63])                     # tiles 0 and 3
+    rec = orc.arm_recall(q, k, lay, orc.SPATIAL, 0, 2, toks)
+    s = q[0, 0, toks] @ k[0, 0, toks].T / 2.0
+    np.testing.assert_allclose(rec[0, 0], scipy.special.expit(
+        [s[0, 0] - s[0, 1], s[1, 1] - s[1, 0]]), atol=1e-15)
+
+
+def test_arm_recall_uniform_logits_and_full_band():
+    lay = orc.Layout(4, 8, 8, 2, 4, 4)
+    z = orc.sizes(lay)
+    r = _rng(61)
+    q, k = (r.standard_normal((1, 2, z["L"], 4)) for _ in range(2))
+    toks = orc.arm_samples(lay, False, 3)
+    full = orc.arm_recall(q, k, lay, orc.TEMPORAL, z["nb"], 2, toks)
+    np.testing.assert_allclose(full, 1.0, atol=1e-14)
+    # zero keys: the recall is the share of sampled keys in kept tiles
+    uni = orc.arm_recall(q, np.zeros_like(k), lay, orc.SPATIAL, 1, 2, toks)
+    tile = [_token_block(lay, z)[t] for t in toks]
+    for a in range(len(toks)):
+        want = sum(abs(tile[a] - tb) <= 1 for tb in tile) / len(toks)
+        np.testing.assert_allclose(uni[0, :, a], want, atol=1e-15)
+
+
+def test_arm_recall_planted_key():
+    lay = orc.Layout(4, 8, 8, 2, 4, 4)
+    z = orc.sizes(lay)
+    r = _rng(67)
+    q, k = (0.1 * r.standard_normal((1, 1, z["L"], 4)) for _ in range(2))
+    toks = orc.arm_samples(lay, False, 2)
+    q[0, 0, 0] = [1.0, 0, 0, 0]
+    far = toks[-1]                                # last frame, far band
+    k[0, 0, far] = [300.0, 0, 0, 0]
+    rec = orc.arm_recall(q, k, lay, orc.SPATIAL, 1, 2, toks)
+    assert rec[0, 0, 0] < 1e-12
+    rec = orc.arm_recall(q, k, lay, orc.SPATIAL, z["nb"], 2, toks)
+    assert rec[0, 0, 0] > 1 - 1e-12
+
+
+def test_arm_classification_order():
+    """Temporal is tested first, then spatial; a mean equal to alpha reaches
+    it (values chosen exact in binary)."""
+    a = 0.75
+    loc = np.array([[[1.0, 0.25], [0.5, 0.5], [0.5, 1.0], [0.25, 0.25]]])
+    glo = np.array([[[0.25, 0.25], [1.0, 0.5], [1.0, 1.0], [0.5, 0.75]]])
+    got = orc.arm_classify(loc, glo, a)
+    assert got.tolist() == [[orc.TEXTURAL, orc.SPATIAL, orc.TEMPORAL, orc.TEXTURAL]]
