@@ -60,7 +60,93 @@ def parse():
                          "(first 10%% of steps dense) on the 720p workload")
     ap.add_argument("--refresh", type=int, default=1,
                     help="with --schedule: predict the mask every R sparse steps")
+    ap.add_argument("--patterns", action="store_true",
+                    help="instead of the step benchmark, time the v1 head-pattern "
+                         "path on the 720p workload: ARM recall and decision, "
+                         "pattern rows, and block-sparse attention on them")
     return ap.parse_args()
+
+
+def _time(fn, reps=5):
+    """Median milliseconds of fn() over reps runs, HIP events on the current
+    stream (the library launches on it)."""
+    import numpy as np
+    import torch
+    fn()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return float(np.median(ts))
+
+
+def pattern_study():
+    """v1 head patterns on the 720p workload (bandwidth 1/4, tau 2, ARM local
+    stride 4 and global stride 64, alpha 0.9): times of each stage and the
+    attention rate on pattern rows, against the 80% predicted mask."""
+    import torch
+
+    from image_diffusion_dits_amd import configs, inputs, rf
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    cfg = configs.VIDEO720
+    q, k, v = inputs.make_qkv(cfg, dev)
+    plan = rf.Plan(cfg.layout)
+    z = plan.sizes
+    B, H, d, bs = cfg.B, cfg.H, cfg.d, z["bs"]
+    qp, qbar = rf.permute_means(plan, q)
+    kp, kbar = rf.permute_means(plan, k)
+    vt = rf.permute(plan, v, order=rf.TILES_T)
+    band, tau, ls, gs, alpha = rf.band_tiles(plan, 0.25), 2, 4, 64, 0.9
+    loc = rf.arm_recall(plan, qp, kp, True, ls, rf.TEMPORAL, band, tau)
+    glo = rf.arm_recall(plan, qp, kp, False, gs, rf.SPATIAL, band, tau)
+    pat, mean = rf.arm_classify(loc, glo, alpha)
+    out = {"metric": "v1 head-pattern path on the 720p workload", "unit": "ms",
+           "higher_is_better": False, "data": "synthetic",
+           "config": {"workload": cfg.name, "heads": H, "band_tiles": band, "tau": tau,
+                      "arm_local_stride": ls, "arm_global_stride": gs, "alpha": alpha,
+                      "arm_local_samples": loc.shape[-1],
+                      "arm_global_samples": glo.shape[-1]}}
+    t_loc = _time(lambda: rf.arm_recall(plan, qp, kp, True, ls, rf.TEMPORAL, band, tau, out=loc))
+    t_glo = _time(lambda: rf.arm_recall(plan, qp, kp, False, gs, rf.SPATIAL, band, tau, out=glo))
+    t_cls = _time(lambda: rf.arm_classify(loc, glo, alpha, pattern=pat, mean=mean))
+    counts = torch.bincount(pat.view(-1).long(), minlength=3).tolist()
+    m = mean.view(-1, 2)
+    out["arm"] = {"ms_local": round(t_loc, 4), "ms_global": round(t_glo, 4),
+                  "ms_classify": round(t_cls, 4),
+                  "heads_spatial_temporal_textural": counts,
+                  "mean_local_recall": round(float(m[:, 0].mean()), 4),
+                  "mean_global_recall": round(float(m[:, 1].mean()), 4)}
+    op = torch.empty_like(qp)
+    runs = {"arm": pat}
+    for name, p in (("spatial", rf.SPATIAL), ("temporal", rf.TEMPORAL),
+                    ("textural", rf.TEXTURAL)):
+        runs[name] = torch.full((B, H), p, dtype=torch.int32, device=dev)
+    width = rf.pattern_row_width(plan.layout, band, tau)
+    rows = torch.empty((B, H, z["n_tiles"], width), dtype=torch.int32, device=dev)
+    out["patterns"] = {}
+    for name, hp in runs.items():
+        t_rows = _time(lambda: rf.pattern_mask(plan, hp, band, tau, out=rows))
+        pairs = int((rows >= 0).sum())
+        t_att = _time(lambda: rf.sparse_attn_rows(plan, qp, kp, vt, rows, out=op))
+        tflop = 4.0 * d * bs * bs * pairs / 1e12
+        out["patterns"][name] = {
+            "ms_rows": round(t_rows, 4), "ms_attn": round(t_att, 3),
+            "kept_pair_share": round(pairs / (B * H * z["n_tiles"] ** 2), 4),
+            "attn_tflops": round(tflop / (t_att * 1e-3), 1),
+            "mfma_frac": round(tflop / (t_att * 1e-3) / PEAK_BF16_TFLOPS, 4)}
+        print(f"[patterns] {name}: {out['patterns'][name]}", file=sys.stderr, flush=True)
+    kept = rf.predict_mask(plan, qbar, kbar, 80)
+    out["predicted_80pct_ms_attn"] = round(
+        _time(lambda: rf.sparse_attn(plan, qp, kp, vt, kept, 80, out=op)), 3)
+    plan.close()
+    print(json.dumps(out))
+    return 0
 
 
 def schedule_study(n_steps, refresh, sparsity):
@@ -226,6 +312,8 @@ def main():
     if a.schedule:
         return schedule_study(a.schedule, a.refresh,
                               a.sparsity if a.sparsity is not None else 80)
+    if a.patterns:
+        return pattern_study()
     if a.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported "
               "(every step is independent per head; the multi-GPU layout is "

@@ -62,12 +62,6 @@ __device__ inline TileJob job_of(int32_t pid, int32_t BH, int32_t nb,
   return {logical / nb, logical % nb};
 }
 
-__device__ inline int64_t row_offset(int32_t tile, int32_t nb,
-                                     int32_t row_len_video, int32_t n_tiles) {
-  return tile < nb ? int64_t(tile) * row_len_video
-                   : int64_t(nb) * row_len_video + int64_t(tile - nb) * n_tiles;
-}
-
 // ---------------------------------------------------------------- bf16 MFMA
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -147,10 +141,10 @@ __global__ __launch_bounds__((BS / 32) * 64, 2) void attn_bf16_kernel(
   const char* vh = reinterpret_cast<const char*>(vt + bh * int64_t(n_tiles) * D * BS);
   // The kept row is read through the constant address space: uniform
   // scalar loads that do not wait on the tile copies in flight.
+  const rf::RowRef rr = rf::row_ref(kept + bh * nnz, qtile, nb, row_len_video, n_tiles);
   const __attribute__((address_space(4))) int32_t* row =
-      (const __attribute__((address_space(4))) int32_t*)(
-          kept + bh * nnz + row_offset(qtile, nb, row_len_video, n_tiles));
-  const int32_t row_len = qtile < nb ? row_len_video : n_tiles;
+      (const __attribute__((address_space(4))) int32_t*)(kept + bh * nnz + rr.offset);
+  const int32_t row_len = rr.len;
 
   // Q operand (B of S^T = K Q^T): lane (li, g) holds q[li][16m + 8g .. +8].
   const int64_t qrow = int64_t(qtile) * BS + wave * 32 + li;
@@ -467,16 +461,16 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
 
   const char* kh = reinterpret_cast<const char*>(kp + bh * Lt * D);
   const char* vh = reinterpret_cast<const char*>(vt + bh * int64_t(n_tiles) * D * BS);
+  const rf::RowRef rr = rf::row_ref(kept + bh * nnz, qtile, nb, row_len_video, n_tiles);
   const __attribute__((address_space(4))) int32_t* row =
-      (const __attribute__((address_space(4))) int32_t*)(
-          kept + bh * nnz + row_offset(qtile, nb, row_len_video, n_tiles));
-  const int32_t row_len = qtile < nb ? row_len_video : n_tiles;
+      (const __attribute__((address_space(4))) int32_t*)(kept + bh * nnz + rr.offset);
+  const int32_t row_len = rr.len;
   const int32_t n_grp = (row_len + 1) / 2;   // tiles per group; group 1 may end on a masked one
   // Kept tile of this group's tile i, or -1: entries past the end and ids out
   // of range are walked as fully masked tiles (whose copies read tile 0).
   auto tile_of = [&](int32_t i) -> int32_t {
     const int32_t j = 2 * i + grp;
-    const int32_t kt = row[min(j, row_len - 1)];
+    const int32_t kt = row[max(min(j, row_len - 1), 0)];
     return (j < row_len && kt >= 0 && kt < n_tiles) ? kt : -1;
   };
 
@@ -727,8 +721,9 @@ __global__ __launch_bounds__(BS) void attn_f32_kernel(
   const int64_t qrow = int64_t(qtile) * BS + t;
   const float* kh = kp + bh * Lt * D;
   const float* vh = vt + bh * int64_t(n_tiles) * D * BS;
-  const int32_t* row = kept + bh * nnz + row_offset(qtile, nb, row_len_video, n_tiles);
-  const int32_t row_len = qtile < nb ? row_len_video : n_tiles;
+  const rf::RowRef rr = rf::row_ref(kept + bh * nnz, qtile, nb, row_len_video, n_tiles);
+  const int32_t* row = kept + bh * nnz + rr.offset;
+  const int32_t row_len = rr.len;
 
   float q[D], o[D];
 #pragma unroll
@@ -793,7 +788,7 @@ __global__ __launch_bounds__(BS) void attn_f32_kernel(
 template <int D, int BS>
 void launch_bf16(const rf_plan* p, const void* qp, const void* kp,
                  const void* vt, const int32_t* kept, void* op, int BH,
-                 const rf_keep& kc, float scale, hipStream_t st) {
+                 int32_t row_len_video, int64_t nnz, float scale, hipStream_t st) {
   const int nb = p->sz.nb, n_tt = p->sz.n_text_tiles;
   dim3 grid(BH * (nb + n_tt));
   if constexpr (BS == 128) {
@@ -801,7 +796,7 @@ void launch_bf16(const rf_plan* p, const void* qp, const void* kp,
                        static_cast<const __bf16*>(qp), static_cast<const __bf16*>(kp),
                        static_cast<const __bf16*>(vt), kept, static_cast<__bf16*>(op),
                        p->tile_bits, p->tile_count, p->sz.Lt, BH, nb, n_tt,
-                       kc.row_len_video, kc.nnz_per_head,
+                       row_len_video, nnz,
                        scale * 1.4426950408889634f);
     return;
   }
@@ -810,21 +805,54 @@ void launch_bf16(const rf_plan* p, const void* qp, const void* kp,
                      static_cast<const __bf16*>(qp), static_cast<const __bf16*>(kp),
                      static_cast<const __bf16*>(vt), kept, static_cast<__bf16*>(op),
                      p->tile_bits, p->tile_count, p->sz.Lt, BH, nb, n_tt,
-                     kc.row_len_video, kc.nnz_per_head,
+                     row_len_video, nnz,
                      scale * 1.4426950408889634f);
 }
 
 template <int D, int BS>
 void launch_f32(const rf_plan* p, const void* qp, const void* kp,
                 const void* vt, const int32_t* kept, void* op, int BH,
-                const rf_keep& kc, float scale, hipStream_t st) {
+                int32_t row_len_video, int64_t nnz, float scale, hipStream_t st) {
   const int nb = p->sz.nb, n_tt = p->sz.n_text_tiles;
   dim3 grid(BH * (nb + n_tt));
   hipLaunchKernelGGL((attn_f32_kernel<D, BS>), grid, dim3(BS), 0, st,
                      static_cast<const float*>(qp), static_cast<const float*>(kp),
                      static_cast<const float*>(vt), kept, static_cast<float*>(op),
                      p->tile_bits, p->tile_count, p->sz.Lt, BH, nb, n_tt,
-                     kc.row_len_video, kc.nnz_per_head, scale);
+                     row_len_video, nnz, scale);
+}
+
+// Shared by both entry points: row_len_video > 0 is the rf_predict_mask
+// layout, row_len_video = -width the padded-row layout.
+rf_status sparse_attn(const rf_plan* plan, const void* qp, const void* kp,
+                      const void* vt, const int32_t* kept_idx,
+                      int32_t row_len_video, int64_t nnz, void* op, int32_t B,
+                      int32_t H, int32_t d, float scale, rf_dtype dtype,
+                      hipStream_t stream, const char* fn) {
+  rf_status st = rf::check_call(plan, B, H, d, dtype, fn);
+  if (st != RF_OK) return st;
+  if (!rf::aligned16(qp) || !rf::aligned16(kp) || !rf::aligned16(vt) ||
+      !rf::aligned16(kept_idx) || !rf::aligned16(op))
+    return rf::fail(RF_ERR_INVALID_ARG, "%s: null or misaligned buffer", fn);
+  if (!(scale > 0.f) || !(scale < 1e30f))
+    return rf::fail(RF_ERR_INVALID_ARG, "%s: scale must be positive and finite", fn);
+  const int BH = B * H;
+  if (int64_t(BH) * plan->sz.n_tiles >= (int64_t(1) << 31))
+    return rf::fail(RF_ERR_UNSUPPORTED, "%s: too many tiles", fn);
+  const int bs = plan->sz.bs;
+  const int32_t rl = row_len_video;
+  if (dtype == RF_BF16) {
+    if (d == 128 && bs == 128) launch_bf16<128, 128>(plan, qp, kp, vt, kept_idx, op, BH, rl, nnz, scale, stream);
+    else if (d == 128 && bs == 64) launch_bf16<128, 64>(plan, qp, kp, vt, kept_idx, op, BH, rl, nnz, scale, stream);
+    else if (d == 64 && bs == 128) launch_bf16<64, 128>(plan, qp, kp, vt, kept_idx, op, BH, rl, nnz, scale, stream);
+    else launch_bf16<64, 64>(plan, qp, kp, vt, kept_idx, op, BH, rl, nnz, scale, stream);
+  } else {
+    if (d == 128 && bs == 128) launch_f32<128, 128>(plan, qp, kp, vt, kept_idx, op, BH, rl, nnz, scale, stream);
+    else if (d == 128 && bs == 64) launch_f32<128, 64>(plan, qp, kp, vt, kept_idx, op, BH, rl, nnz, scale, stream);
+    else if (d == 64 && bs == 128) launch_f32<64, 128>(plan, qp, kp, vt, kept_idx, op, BH, rl, nnz, scale, stream);
+    else launch_f32<64, 64>(plan, qp, kp, vt, kept_idx, op, BH, rl, nnz, scale, stream);
+  }
+  return rf::check_launch(fn);
 }
 
 }  // namespace
@@ -835,30 +863,25 @@ extern "C" rf_status rf_sparse_attn(const rf_plan* plan, const void* qp,
                                     int32_t sparsity_pct, void* op, int32_t B,
                                     int32_t H, int32_t d, float scale,
                                     rf_dtype dtype, hipStream_t stream) {
-  rf_status st = rf::check_call(plan, B, H, d, dtype, "rf_sparse_attn");
-  if (st != RF_OK) return st;
-  if (!rf::aligned16(qp) || !rf::aligned16(kp) || !rf::aligned16(vt) ||
-      !rf::aligned16(kept_idx) || !rf::aligned16(op))
-    return rf::fail(RF_ERR_INVALID_ARG, "rf_sparse_attn: null or misaligned buffer");
-  if (!(scale > 0.f) || !(scale < 1e30f))
-    return rf::fail(RF_ERR_INVALID_ARG, "rf_sparse_attn: scale must be positive and finite");
+  if (plan == nullptr) return rf::fail(RF_ERR_INVALID_ARG, "rf_sparse_attn: null plan");
   rf_keep kc;
-  st = rf_keep_count(&plan->lay, sparsity_pct, &kc);
+  rf_status st = rf_keep_count(&plan->lay, sparsity_pct, &kc);
   if (st != RF_OK) return st;
-  const int BH = B * H;
-  if (int64_t(BH) * plan->sz.n_tiles >= (int64_t(1) << 31))
-    return rf::fail(RF_ERR_UNSUPPORTED, "rf_sparse_attn: too many tiles");
-  const int bs = plan->sz.bs;
-  if (dtype == RF_BF16) {
-    if (d == 128 && bs == 128) launch_bf16<128, 128>(plan, qp, kp, vt, kept_idx, op, BH, kc, scale, stream);
-    else if (d == 128 && bs == 64) launch_bf16<128, 64>(plan, qp, kp, vt, kept_idx, op, BH, kc, scale, stream);
-    else if (d == 64 && bs == 128) launch_bf16<64, 128>(plan, qp, kp, vt, kept_idx, op, BH, kc, scale, stream);
-    else launch_bf16<64, 64>(plan, qp, kp, vt, kept_idx, op, BH, kc, scale, stream);
-  } else {
-    if (d == 128 && bs == 128) launch_f32<128, 128>(plan, qp, kp, vt, kept_idx, op, BH, kc, scale, stream);
-    else if (d == 128 && bs == 64) launch_f32<128, 64>(plan, qp, kp, vt, kept_idx, op, BH, kc, scale, stream);
-    else if (d == 64 && bs == 128) launch_f32<64, 128>(plan, qp, kp, vt, kept_idx, op, BH, kc, scale, stream);
-    else launch_f32<64, 64>(plan, qp, kp, vt, kept_idx, op, BH, kc, scale, stream);
-  }
-  return rf::check_launch("rf_sparse_attn");
+  return sparse_attn(plan, qp, kp, vt, kept_idx, kc.row_len_video, kc.nnz_per_head,
+                     op, B, H, d, scale, dtype, stream, "rf_sparse_attn");
+}
+
+extern "C" rf_status rf_sparse_attn_rows(const rf_plan* plan, const void* qp,
+                                         const void* kp, const void* vt,
+                                         const int32_t* kept_rows,
+                                         int32_t row_width, void* op, int32_t B,
+                                         int32_t H, int32_t d, float scale,
+                                         rf_dtype dtype, hipStream_t stream) {
+  if (plan == nullptr) return rf::fail(RF_ERR_INVALID_ARG, "rf_sparse_attn_rows: null plan");
+  if (row_width < 1 || row_width > plan->sz.n_tiles)
+    return rf::fail(RF_ERR_INVALID_ARG, "rf_sparse_attn_rows: row_width %d outside [1, %d]",
+                    row_width, plan->sz.n_tiles);
+  return sparse_attn(plan, qp, kp, vt, kept_rows, -row_width,
+                     int64_t(plan->sz.n_tiles) * row_width, op, B, H, d, scale,
+                     dtype, stream, "rf_sparse_attn_rows");
 }

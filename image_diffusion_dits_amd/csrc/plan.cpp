@@ -10,6 +10,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "rf_internal.h"
@@ -90,10 +91,34 @@ int64_t slot_of(const rf_layout& lay, const rf_sizes& sz, const Geometry& g,
 }
 
 struct HostTables {
-  std::vector<int32_t> slot_src, tok_slot, tile_count;
+  std::vector<int32_t> slot_src, tok_slot, tile_count, tile_rank;
   std::vector<uint32_t> tile_bits;
   std::vector<uint8_t> is_sink;
 };
+
+// Position of each video tile when the tiles are sorted by (h, w, t) of
+// their first valid token: the spatial-major order in which the temporal
+// head pattern of the v1 page (RainFusion review, "What carries the
+// argument": temporal heads attend to one local region across frames) is a
+// band.  With the window order this is (bh, bw, bt) order.
+void build_rank(const rf_layout& lay, const rf_sizes& sz,
+                const std::vector<int32_t>& slot_src, std::vector<int32_t>* rank) {
+  struct Key { int64_t h, w, t; int32_t tile; };
+  std::vector<Key> keys(sz.nb);
+  const int64_t hw = int64_t(lay.H) * lay.W;
+  for (int32_t i = 0; i < sz.nb; ++i) {
+    int64_t n = -1;
+    for (int32_t s = 0; s < sz.bs && n < 0; ++s) n = slot_src[int64_t(i) * sz.bs + s];
+    keys[i] = {(n % hw) / lay.W, n % lay.W, n / hw, i};
+  }
+  std::sort(keys.begin(), keys.end(), [](const Key& a, const Key& b) {
+    if (a.h != b.h) return a.h < b.h;
+    if (a.w != b.w) return a.w < b.w;
+    return a.t < b.t;
+  });
+  rank->assign(sz.nb, 0);
+  for (int32_t r = 0; r < sz.nb; ++r) (*rank)[keys[r].tile] = r;
+}
 
 void build_tables(const rf_layout& lay, const rf_sizes& sz, const Geometry& g,
                   HostTables* t) {
@@ -122,6 +147,7 @@ void build_tables(const rf_layout& lay, const rf_sizes& sz, const Geometry& g,
     for (int64_t n = 0; n < int64_t(lay.H) * lay.W; ++n)
       t->is_sink[t->tok_slot[n] / sz.bs] = 1;
   }
+  build_rank(lay, sz, t->slot_src, &t->tile_rank);
 }
 
 }  // namespace
@@ -215,6 +241,51 @@ rf_status rf_keep_count(const rf_layout* lay, int32_t sparsity_pct,
   return RF_OK;
 }
 
+rf_status rf_tile_rank(const rf_layout* lay, int32_t* rank, int64_t cap) {
+  rf_sizes sz;
+  Geometry g;
+  rf_status st = compute_sizes(lay, &sz, &g);
+  if (st != RF_OK) return st;
+  if (rank == nullptr) return rf::fail(RF_ERR_INVALID_ARG, "rf_tile_rank: null buffer");
+  if (cap < sz.nb)
+    return rf::fail(RF_ERR_BUFFER_TOO_SMALL, "rf_tile_rank: need %d elements", sz.nb);
+  HostTables t;
+  build_tables(*lay, sz, g, &t);
+  memcpy(rank, t.tile_rank.data(), sizeof(int32_t) * sz.nb);
+  return RF_OK;
+}
+
+rf_status rf_pattern_row_width(const rf_layout* lay, int32_t band, int32_t tau,
+                               int32_t* width) {
+  rf_sizes sz;
+  rf_status st = compute_sizes(lay, &sz, nullptr);
+  if (st != RF_OK) return st;
+  if (width == nullptr)
+    return rf::fail(RF_ERR_INVALID_ARG, "rf_pattern_row_width: null output");
+  if (band < 0 || tau < 1)
+    return rf::fail(RF_ERR_INVALID_ARG, "band %d must be >= 0 and tau %d >= 1", band, tau);
+  // Longest video row: a band row keeps at most 2*band + 1 tiles, a
+  // checkerboard row at most ceil(nb / tau); text tiles follow.
+  const int64_t b = std::min<int64_t>(2 * int64_t(band) + 1, sz.nb);
+  const int64_t c = ceil_div(sz.nb, tau);
+  int64_t w = std::max(b, c) + sz.n_text_tiles;
+  if (sz.n_text_tiles > 0) w = std::max<int64_t>(w, sz.n_tiles);
+  *width = int32_t(w);
+  return RF_OK;
+}
+
+rf_status rf_arm_sample_count(const rf_layout* lay, int32_t local,
+                              int32_t stride, int32_t* n) {
+  rf_sizes sz;
+  rf_status st = compute_sizes(lay, &sz, nullptr);
+  if (st != RF_OK) return st;
+  if (n == nullptr) return rf::fail(RF_ERR_INVALID_ARG, "rf_arm_sample_count: null output");
+  if (stride < 1) return rf::fail(RF_ERR_INVALID_ARG, "ARM stride %d must be >= 1", stride);
+  const int64_t limit = local ? int64_t(lay->H) * lay->W : sz.N;
+  *n = int32_t(ceil_div(limit, stride));
+  return RF_OK;
+}
+
 const char* rf_status_str(rf_status s) {
   switch (s) {
     case RF_OK: return "ok";
@@ -238,6 +309,7 @@ void rf_plan_destroy(rf_plan* p) {
   (void)hipFree(p->tile_bits);
   (void)hipFree(p->tile_count);
   (void)hipFree(p->is_sink);
+  (void)hipFree(p->tile_rank);
   if (cur >= 0 && cur != p->device) (void)hipSetDevice(cur);
   delete p;
 }
@@ -268,6 +340,7 @@ rf_status rf_plan_create(const rf_layout* lay, rf_plan** out) {
       {(void**)&p->tile_bits, t.tile_bits.data(), sizeof(uint32_t) * t.tile_bits.size()},
       {(void**)&p->tile_count, t.tile_count.data(), sizeof(int32_t) * t.tile_count.size()},
       {(void**)&p->is_sink, t.is_sink.data(), t.is_sink.size()},
+      {(void**)&p->tile_rank, t.tile_rank.data(), sizeof(int32_t) * t.tile_rank.size()},
   };
   for (const Item& it : items) {
     e = hipMalloc(it.dst, it.bytes > 0 ? it.bytes : 4);

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librf.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_BUFFER_TOO_SMALL = range(5)
 F32, BF16 = 0, 1
 ROWS, TILES_T = 0, 1
+SPATIAL, TEMPORAL, TEXTURAL = 0, 1, 2
 
 _c_i32, _c_i64, _c_f32, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
 
@@ -71,6 +72,20 @@ _SIGNATURES = {
                        _c_i32, _c_f32, ctypes.c_int, _vp],
     "rf_attention_recall": [_vp, _vp, _vp, _vp, _c_i32, _vp, _c_i32, _c_i32,
                             _c_i32, _c_i32, _c_f32, ctypes.c_int, _vp, _vp],
+    "rf_tile_rank": [_P(Layout), _vp, _c_i64],
+    "rf_pattern_row_width": [_P(Layout), _c_i32, _c_i32, _P(_c_i32)],
+    "rf_arm_sample_count": [_P(Layout), _c_i32, _c_i32, _P(_c_i32)],
+    "rf_sparse_attn_rows": [_vp, _vp, _vp, _vp, _vp, _c_i32, _vp, _c_i32,
+                            _c_i32, _c_i32, _c_f32, ctypes.c_int, _vp],
+    "rf_attention_recall_rows": [_vp, _vp, _vp, _vp, _c_i32, _vp, _c_i32,
+                                 _c_i32, _c_i32, _c_i32, _c_f32, ctypes.c_int,
+                                 _vp, _vp],
+    "rf_pattern_mask": [_vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _c_i32,
+                        _vp],
+    "rf_arm_recall": [_vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                      _c_i32, _c_i32, _c_i32, _c_f32, ctypes.c_int, _vp, _vp],
+    "rf_arm_classify": [_vp, _c_i32, _vp, _c_i32, _c_i32, _c_f32, _vp, _vp,
+                        _vp],
 }
 
 _lib = None
@@ -145,6 +160,31 @@ def keep_count(lay, sparsity_pct):
     _check(lib().rf_keep_count(ctypes.byref(_as_layout(lay)), int(sparsity_pct),
                                ctypes.byref(out)), "rf_keep_count")
     return out.as_dict()
+
+
+def tile_rank(lay):
+    """Position of each video tile in spatial-major order (numpy int32)."""
+    lay = _as_layout(lay)
+    out = np.empty(layout_sizes(lay)["nb"], np.int32)
+    _check(lib().rf_tile_rank(ctypes.byref(lay), out.ctypes.data, out.size),
+           "rf_tile_rank")
+    return out
+
+
+def pattern_row_width(lay, band, tau):
+    w = _c_i32()
+    _check(lib().rf_pattern_row_width(ctypes.byref(_as_layout(lay)), int(band),
+                                      int(tau), ctypes.byref(w)),
+           "rf_pattern_row_width")
+    return w.value
+
+
+def arm_sample_count(lay, local, stride):
+    n = _c_i32()
+    _check(lib().rf_arm_sample_count(ctypes.byref(_as_layout(lay)), int(bool(local)),
+                                     int(stride), ctypes.byref(n)),
+           "rf_arm_sample_count")
+    return n.value
 
 
 # ---------------------------------------------------------------- plan
@@ -310,6 +350,116 @@ def attention_recall(plan, qp, kp, kept, sparsity_pct, sample_tiles, scale=None,
                                      d, float(scale), _dtype_code(qp), _ptr(out),
                                      _stream()),
            "rf_attention_recall")
+    return out
+
+
+def sparse_attn_rows(plan, qp, kp, vt, rows, scale=None, out=None):
+    """rf_sparse_attn on padded kept rows: rows is int32 [B, H, n_tiles, width]."""
+    B, H, d = _bhd(qp)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(qp)
+    _check(lib().rf_sparse_attn_rows(plan.handle, _ptr(qp), _ptr(kp), _ptr(vt),
+                                     _ptr(rows), rows.shape[-1], _ptr(out), B, H,
+                                     d, float(scale), _dtype_code(qp), _stream()),
+           "rf_sparse_attn_rows")
+    return out
+
+
+def attention_recall_rows(plan, qp, kp, rows, sample_tiles, scale=None, out=None):
+    """rf_attention_recall on padded kept rows [B, H, n_tiles, width]."""
+    B, H, d = _bhd(qp)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    n = sample_tiles.numel()
+    if out is None:
+        out = torch.empty((B, H, n, plan.sizes["bs"]), dtype=torch.float32,
+                          device=qp.device)
+    _check(lib().rf_attention_recall_rows(plan.handle, _ptr(qp), _ptr(kp), _ptr(rows),
+                                          rows.shape[-1], _ptr(sample_tiles), n, B,
+                                          H, d, float(scale), _dtype_code(qp),
+                                          _ptr(out), _stream()),
+           "rf_attention_recall_rows")
+    return out
+
+
+def band_tiles(plan, bandwidth):
+    """Band half-width in tiles for a bandwidth fraction: floor(b nb + 1/2)."""
+    return int(math.floor(bandwidth * plan.sizes["nb"] + 0.5))
+
+
+def pattern_mask(plan, head_pattern, band, tau=2, width=None, out=None):
+    """Padded kept rows [B, H, n_tiles, width] of the v1 head patterns.
+    head_pattern: int32 [B, H] on the device."""
+    B, H = head_pattern.shape
+    if width is None:
+        width = pattern_row_width(plan.layout, band, tau)
+    if out is None:
+        out = torch.empty((B, H, plan.sizes["n_tiles"], width), dtype=torch.int32,
+                          device=head_pattern.device)
+    _check(lib().rf_pattern_mask(plan.handle, _ptr(head_pattern.contiguous()), B, H,
+                                 int(band), int(tau), _ptr(out), out.shape[-1],
+                                 _stream()), "rf_pattern_mask")
+    return out
+
+
+def arm_recall(plan, qp, kp, local, stride, pattern, band, tau=2, scale=None,
+               out=None):
+    """Per sampled query, the share of its mass over the sampled keys that
+    the pattern keeps: fp32 [B, H, n]."""
+    B, H, d = _bhd(qp)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    n = arm_sample_count(plan.layout, local, stride)
+    if out is None:
+        out = torch.empty((B, H, n), dtype=torch.float32, device=qp.device)
+    _check(lib().rf_arm_recall(plan.handle, _ptr(qp), _ptr(kp), int(bool(local)),
+                               int(stride), int(pattern), int(band), int(tau), B, H,
+                               d, float(scale), _dtype_code(qp), _ptr(out),
+                               _stream()), "rf_arm_recall")
+    return out
+
+
+def arm_classify(local_recall, global_recall, alpha=0.9, pattern=None, mean=None):
+    """Head patterns (int32 [B, H]) and mean recalls (fp32 [B, H, 2]) from
+    the two recall samples [B, H, n_local] and [B, H, n_global]."""
+    B, H, nl = local_recall.shape
+    ng = global_recall.shape[-1]
+    if pattern is None:
+        pattern = torch.empty((B, H), dtype=torch.int32, device=local_recall.device)
+    if mean is None:
+        mean = torch.empty((B, H, 2), dtype=torch.float32, device=local_recall.device)
+    _check(lib().rf_arm_classify(_ptr(local_recall), nl, _ptr(global_recall), ng,
+                                 B * H, float(alpha), _ptr(pattern), _ptr(mean),
+                                 _stream()), "rf_arm_classify")
+    return pattern, mean
+
+
+def arm_patterns(plan, qp, kp, band, local_stride, global_stride, alpha=0.9,
+                 tau=2, scale=None):
+    """The v1 classifier: recall of the temporal mask on the local sample and
+    of the spatial mask on the global sample, then the decision.  Returns
+    (head_pattern [B, H], mean recalls [B, H, 2])."""
+    loc = arm_recall(plan, qp, kp, True, local_stride, TEMPORAL, band, tau, scale)
+    glo = arm_recall(plan, qp, kp, False, global_stride, SPATIAL, band, tau, scale)
+    return arm_classify(loc, glo, alpha)
+
+
+def padded_rows(rows):
+    """Per-row arrays of padded kept rows [B, H, n_tiles, width] (host copy),
+    each cut at its first negative entry."""
+    r = rows.detach().cpu().numpy()
+    out = []
+    for b in range(r.shape[0]):
+        per_head = []
+        for h in range(r.shape[1]):
+            rr = []
+            for row in r[b, h]:
+                neg = np.flatnonzero(row < 0)
+                rr.append(row[:neg[0]] if len(neg) else row)
+            per_head.append(rr)
+        out.append(per_head)
     return out
 
 

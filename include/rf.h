@@ -11,7 +11,9 @@
  *         blockwise representative tokens); Figure 2 and 3 captions.
  *   [RF1] "RainFusion: Adaptive Video Generation Acceleration via
  *         Multi-Dimensional Visual Redundancy" (arXiv 2505.21036): Abstract;
- *         review page, Assumptions (softmax attention, Eq. (1)).
+ *         review page, Assumptions (softmax attention, Eq. (1)), "What
+ *         carries the argument" and "Core claim" (head patterns, ARM),
+ *         free parameters (bandwidth, stride tau, threshold alpha).
  *
  * One attention call of a diffusion transformer runs, on the caller's HIP
  * stream:
@@ -21,6 +23,10 @@
  *   rf_predict_mask(Qbar, Kbar)                                kept tiles
  *   rf_sparse_attn(Qp, Kp, Vt, kept)                           Op
  *   rf_unpermute(Op)                                           O
+ * With the v1 head patterns in place of the predicted mask:
+ *   rf_arm_recall(local, temporal), rf_arm_recall(global, spatial),
+ *   rf_arm_classify -> head patterns; rf_pattern_mask -> kept rows;
+ *   rf_sparse_attn_rows(Qp, Kp, Vt, rows) -> Op.
  *
  * Conventions
  *   Token tensors are contiguous [B][H][tokens][d] (RF_ROWS).  Raster token
@@ -63,6 +69,19 @@ typedef enum {
 } rf_status;
 
 typedef enum { RF_F32 = 0, RF_BF16 = 1 } rf_dtype;
+
+/* Head patterns of RainFusion v1 [RF1 review, "What carries the argument"],
+ * as tile masks.  Band half-width `band` (tiles) and checkerboard stride
+ * `tau` are parameters; bandwidth b maps to band = floor(b*nb + 1/2), and
+ * b = 1/4 keeps 1 - (3/4)^2 = 7/16 of the video tile pairs.
+ *   RF_SPATIAL   video tile i keeps video tile j when |i - j| <= band
+ *                (tiles in frame-major order, the block index);
+ *   RF_TEMPORAL  |r(i) - r(j)| <= band, r = position of the tile when the
+ *                tiles are sorted by (h, w, t) of their first valid token;
+ *   RF_TEXTURAL  j = i (mod tau).
+ * Text tiles are appended to every video row; text query rows keep every
+ * tile. */
+typedef enum { RF_SPATIAL = 0, RF_TEMPORAL = 1, RF_TEXTURAL = 2 } rf_pattern;
 
 /* Order of a permuted tensor in memory. */
 typedef enum {
@@ -131,6 +150,22 @@ rf_status rf_layout_tables(const rf_layout* lay, int32_t* slot_src,
  * Figure 2: 60% for image editing]. */
 rf_status rf_keep_count(const rf_layout* lay, int32_t sparsity_pct,
                         rf_keep* out);
+
+/* r(i) of RF_TEMPORAL for every video tile, into a host buffer of at least
+ * nb elements (a permutation of 0..nb-1). */
+rf_status rf_tile_rank(const rf_layout* lay, int32_t* rank, int64_t cap);
+
+/* Row width that holds every row of the pattern masks for (band, tau):
+ * max(min(2*band + 1, nb), ceil(nb/tau)) + n_text_tiles, or n_tiles when
+ * there is text.  band >= 0, tau >= 1. */
+rf_status rf_pattern_row_width(const rf_layout* lay, int32_t band, int32_t tau,
+                               int32_t* width);
+
+/* Number of ARM samples: ceil(H*W / stride) for the local sample (every
+ * stride-th raster token of frame 0, local != 0) or ceil(N / stride) for
+ * the global one (every stride-th video token).  stride >= 1. */
+rf_status rf_arm_sample_count(const rf_layout* lay, int32_t local,
+                              int32_t stride, int32_t* n);
 
 const char* rf_status_str(rf_status s);
 const char* rf_last_error(void);
@@ -229,6 +264,67 @@ rf_status rf_attention_recall(const rf_plan* plan, const void* qp,
                               int32_t B, int32_t H, int32_t d, float scale,
                               rf_dtype dtype, float* recall,
                               hipStream_t stream);
+
+/* ---- padded kept rows and the v1 head patterns ------------------------- */
+
+/* Kept rows in the padded layout: int32 [B][H][n_tiles][row_width], row t
+ * of a head holding the kept tile ids of query tile t in ascending order
+ * followed by -1 up to row_width (the length of a row is the position of
+ * its first negative entry; an empty row gives output 0).  Entries outside
+ * [0, n_tiles) before the first -1 are skipped.  1 <= row_width <= n_tiles.
+ * Otherwise identical to rf_sparse_attn / rf_attention_recall. */
+rf_status rf_sparse_attn_rows(const rf_plan* plan, const void* qp,
+                              const void* kp, const void* vt,
+                              const int32_t* kept_rows, int32_t row_width,
+                              void* op, int32_t B, int32_t H, int32_t d,
+                              float scale, rf_dtype dtype, hipStream_t stream);
+rf_status rf_attention_recall_rows(const rf_plan* plan, const void* qp,
+                                   const void* kp, const int32_t* kept_rows,
+                                   int32_t row_width,
+                                   const int32_t* sample_tiles,
+                                   int32_t n_sample, int32_t B, int32_t H,
+                                   int32_t d, float scale, rf_dtype dtype,
+                                   float* recall, hipStream_t stream);
+
+/* Head-pattern mask [RF1 review, "What carries the argument": striped
+ * bands for spatial and temporal heads, checkerboard for textural heads]:
+ * writes the padded kept rows (layout above) of every (b, h) from its
+ * pattern head_pattern[b*H + h] (device int32, an rf_pattern; any other
+ * value gives empty video rows).  row_width must lie in
+ * [rf_pattern_row_width(band, tau), n_tiles]; kept_rows holds
+ * B*H*n_tiles*row_width int32. */
+rf_status rf_pattern_mask(const rf_plan* plan, const int32_t* head_pattern,
+                          int32_t B, int32_t H, int32_t band, int32_t tau,
+                          int32_t* kept_rows, int32_t row_width,
+                          hipStream_t stream);
+
+/* ARM recall [RF1 review, "What carries the argument": R' = S(Q', K', M') /
+ * S(Q', K', M_init) on sampled queries and keys; "Core claim": first-frame
+ * tokens for the local pattern, equally spaced tokens for the global one].
+ * The sample is every stride-th raster token of frame 0 (local != 0) or of
+ * the video; sampled tokens are both the queries and the keys.  For sampled
+ * query a: recall[b][h][a] = sum of exp(scale * q_a . k_b) over the sampled
+ * keys b whose tile the query's tile keeps under `pattern` (band, tau),
+ * divided by the same sum over all sampled keys.  fp32 arithmetic (bf16 or
+ * fp32 operands).  qp, kp: [B][H][Lt][d] RF_ROWS; recall: fp32
+ * [B][H][n], n from rf_arm_sample_count.  d in {64, 128}. */
+rf_status rf_arm_recall(const rf_plan* plan, const void* qp, const void* kp,
+                        int32_t local, int32_t stride, int32_t pattern,
+                        int32_t band, int32_t tau, int32_t B, int32_t H,
+                        int32_t d, float scale, rf_dtype dtype, float* recall,
+                        hipStream_t stream);
+
+/* ARM decision [RF1 review, "Core claim": temporal first, then spatial,
+ * otherwise textural]: per head bh < BH, bR = mean of local_recall[bh][:]
+ * (n_local values, recall of the temporal mask on the local sample) and
+ * eR = mean of global_recall[bh][:] (the spatial mask on the global
+ * sample), fp32; head_pattern[bh] = RF_TEMPORAL if bR >= alpha, else
+ * RF_SPATIAL if eR >= alpha, else RF_TEXTURAL.  mean_or_null: optional fp32
+ * [BH][2] = (bR, eR).  All buffers on the device. */
+rf_status rf_arm_classify(const float* local_recall, int32_t n_local,
+                          const float* global_recall, int32_t n_global,
+                          int32_t BH, float alpha, int32_t* head_pattern,
+                          float* mean_or_null, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -134,7 +134,17 @@ def test_gpu_entry_points_reject_bad_arguments_without_a_device():
                             rf.BF16, None) == rf.ERR_INVALID_ARG
     assert L.rf_attention_recall(None, buf, buf, buf, 50, buf, 1, 1, 1, 64, 0.125,
                                  rf.BF16, buf, None) == rf.ERR_INVALID_ARG
+    assert L.rf_sparse_attn_rows(None, buf, buf, buf, buf, 4, buf, 1, 1, 64, 0.125,
+                                 rf.BF16, None) == rf.ERR_INVALID_ARG
+    assert L.rf_attention_recall_rows(None, buf, buf, buf, 4, buf, 1, 1, 1, 64,
+                                      0.125, rf.BF16, buf, None) == rf.ERR_INVALID_ARG
+    assert L.rf_pattern_mask(None, buf, 1, 1, 2, 2, buf, 8, None) == rf.ERR_INVALID_ARG
+    assert L.rf_arm_recall(None, buf, buf, 1, 4, rf.TEMPORAL, 2, 2, 1, 1, 64, 0.125,
+                           rf.BF16, buf, None) == rf.ERR_INVALID_ARG
     assert b"null plan" in L.rf_last_error()
+    # The classifier needs no plan: its sizes are checked first.
+    assert L.rf_arm_classify(buf, 0, buf, 4, 1, 0.9, buf, None, None) == rf.ERR_INVALID_ARG
+    assert L.rf_arm_classify(None, 4, buf, 4, 1, 0.9, buf, None, None) == rf.ERR_INVALID_ARG
     assert L.rf_plan_sizes(None, None) == rf.ERR_INVALID_ARG
     L.rf_plan_destroy(None)  # no-op
     assert L.rf_status_str(rf.ERR_HIP) == b"HIP runtime error"
@@ -147,3 +157,40 @@ def test_plan_create_without_device_reports_hip_error():
     with pytest.raises(rf.RfError) as e:
         rf.Plan(configs.TINY.layout)
     assert e.value.status == rf.ERR_HIP
+
+
+@pytest.mark.parametrize("lay", LAYOUTS)
+def test_tile_rank_matches_oracle(lay):
+    np.testing.assert_array_equal(rf.tile_rank(lay), orc.tile_rank(_olay(rf._as_layout(lay))))
+
+
+@pytest.mark.parametrize("lay", LAYOUTS)
+@pytest.mark.parametrize("b,tau", [(0.0, 1), (0.25, 2), (0.1, 3), (1.0, 4)])
+def test_pattern_row_width_holds_the_longest_oracle_row(lay, b, tau):
+    """The width is the longest row of the three oracle masks."""
+    olay = _olay(rf._as_layout(lay))
+    w = orc.band_halfwidth(olay, b)
+    longest = 0
+    for p in (orc.SPATIAL, orc.TEMPORAL, orc.TEXTURAL):
+        rows = orc.pattern_mask(olay, np.array([[p]]), w, tau)[0][0]
+        longest = max(longest, max(len(r) for r in rows))
+    assert rf.pattern_row_width(lay, w, tau) == longest
+
+
+@pytest.mark.parametrize("lay", LAYOUTS)
+@pytest.mark.parametrize("stride", [1, 3, 64])
+def test_arm_sample_count_matches_oracle(lay, stride):
+    olay = _olay(rf._as_layout(lay))
+    for local in (True, False):
+        assert rf.arm_sample_count(lay, local, stride) == len(orc.arm_samples(olay, local, stride))
+
+
+def test_pattern_helpers_reject_bad_parameters():
+    lay = rf._as_layout(configs.TINY.layout)
+    w, n = ctypes.c_int32(), ctypes.c_int32()
+    L = rf.lib()
+    assert L.rf_pattern_row_width(ctypes.byref(lay), -1, 2, ctypes.byref(w)) == rf.ERR_INVALID_ARG
+    assert L.rf_pattern_row_width(ctypes.byref(lay), 1, 0, ctypes.byref(w)) == rf.ERR_INVALID_ARG
+    assert L.rf_arm_sample_count(ctypes.byref(lay), 1, 0, ctypes.byref(n)) == rf.ERR_INVALID_ARG
+    small = np.empty(1, np.int32)
+    assert L.rf_tile_rank(ctypes.byref(lay), small.ctypes.data, 1) == rf.ERR_BUFFER_TOO_SMALL

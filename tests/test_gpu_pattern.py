@@ -1,0 +1,328 @@
+"""Parity of the v1 head-pattern path (through the C-ABI) with the fp64 oracle:
+pattern masks bit-exact, block-sparse attention on padded kept rows within
+the attention tolerance of parity.py, ARM recall within the recall
+tolerance (fp32 sums with a running maximum against fp64: 2e-5 absolute up
+to 10k sampled keys), and the ARM decision equal to the oracle's wherever a
+head's mean recall is not within 1e-4 of alpha.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import parity
+from image_diffusion_dits_amd import configs, inputs, rf
+from oracle import rainfusion_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+PATTERNS = (orc.SPATIAL, orc.TEMPORAL, orc.TEXTURAL)
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _iid(shape, seed, dtype):
+    return inputs.random_tensor(shape, seed, device="cuda", dtype=dtype)
+
+
+def _head_patterns(B, H, seed):
+    """Every pattern at least once when B*H >= 3, the rest random."""
+    rng = np.random.default_rng(seed)
+    hp = rng.integers(0, 3, size=B * H)
+    hp[:min(3, B * H)] = PATTERNS[:min(3, B * H)]
+    return hp.reshape(B, H).astype(np.int32)
+
+
+def check_rows_attention(lay_dict, q, k, v, hp, band, tau, dtype, sample_tiles=None,
+                         seed=0):
+    """Pattern rows bit-exact against the oracle, then attention on them for
+    every query tile (sample_tiles None) or a random subset per head."""
+    lay = parity.olayout(lay_dict)
+    z = orc.sizes(lay)
+    plan = rf.Plan(lay_dict)
+    qp, kp = rf.permute(plan, q), rf.permute(plan, k)
+    vt = rf.permute(plan, v, order=rf.TILES_T)
+    rows = rf.pattern_mask(plan, torch.tensor(hp, device="cuda"), band, tau)
+    op = rf.sparse_attn_rows(plan, qp, kp, vt, rows)
+    torch.cuda.synchronize()
+    width = rows.shape[-1]
+    assert width == rf.pattern_row_width(lay_dict, band, tau)
+    want_rows = orc.pattern_mask(lay, hp, band, tau)
+    raw = rows.cpu().numpy()
+    got_rows = rf.padded_rows(rows)
+    B, H = hp.shape
+    Lp = z["Lp"]
+    valid = orc.slot_valid(lay)
+    rng = np.random.default_rng(seed)
+    worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            for i in range(z["n_tiles"]):
+                w, g = want_rows[b][h][i], got_rows[b][h][i]
+                assert g.tolist() == w.tolist(), f"row b{b} h{h} tile {i} pattern {hp[b, h]}"
+                assert np.all(raw[b, h, i, len(g):] == -1), f"padding b{b} h{h} tile {i}"
+            tiles = (range(z["n_tiles"]) if sample_tiles is None else
+                     sorted(rng.choice(z["n_tiles"], size=min(sample_tiles, z["n_tiles"]),
+                                       replace=False).tolist()))
+            want = orc.sparse_attention(parity.values(qp[b:b + 1, h:h + 1, :Lp]),
+                                        parity.values(kp[b:b + 1, h:h + 1, :Lp]),
+                                        orc.permute(parity.values(v[b:b + 1, h:h + 1]), lay),
+                                        [[want_rows[b][h]]], lay,
+                                        query_tiles={(0, 0): tiles})
+            mx, _ = parity.check_attention(parity.values(op[b, h, :Lp]), want[0, 0],
+                                           valid, dtype)
+            worst = max(worst, mx)
+    say(f"  rows width={width} exact; attention max_abs={worst:.3e}")
+    plan.close()
+    return rows, op
+
+
+EDGE = [
+    # name, layout, B, H, d, dtype, bandwidth, tau
+    ("ragged3d-text77", dict(T=3, H=13, W=21, wt=2, wh=8, ww=8, n_text=77,
+                             permute=1, sink=0), 2, 3, 128, torch.bfloat16, 0.25, 2),
+    ("bs64-d64", dict(T=2, H=10, W=9, wt=1, wh=8, ww=8, n_text=0, permute=1,
+                      sink=0), 1, 3, 64, torch.bfloat16, 0.25, 3),
+    ("raster-bs64-text10", dict(T=3, H=7, W=11, wt=1, wh=8, ww=8, n_text=10,
+                                permute=0, sink=0), 1, 3, 128, torch.bfloat16, 0.3, 2),
+    ("f32-d128-bs128", dict(T=2, H=9, W=17, wt=2, wh=8, ww=8, n_text=5,
+                            permute=1, sink=0), 1, 3, 128, torch.float32, 0.25, 2),
+    ("f32-d64-bs64-raster", dict(T=2, H=5, W=30, wt=1, wh=8, ww=8, n_text=64,
+                                 permute=0, sink=0), 1, 3, 64, torch.float32, 0.1, 4),
+    ("single-block", dict(T=1, H=8, W=8, wt=1, wh=8, ww=8, n_text=0, permute=1,
+                          sink=0), 1, 3, 128, torch.bfloat16, 0.25, 2),
+    ("band0-tau1", dict(T=3, H=13, W=21, wt=2, wh=8, ww=8, n_text=0, permute=1,
+                        sink=0), 1, 3, 128, torch.bfloat16, 0.0, 1),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
+def test_pattern_rows_and_attention_edge_layouts(case):
+    name, lay, B, H, d, dt, bw, tau = case
+    say(f"[pattern edge] {name} B={B} H={H} d={d} {dt} b={bw} tau={tau}")
+    L = rf.layout_sizes(lay)["L"]
+    q, k, v = (_iid((B, H, L, d), s, dt) for s in (41, 42, 43))
+    band = orc.band_halfwidth(parity.olayout(lay), bw)
+    check_rows_attention(lay, q, k, v, _head_patterns(B, H, 5), band, tau,
+                         "bf16" if dt == torch.bfloat16 else "f32")
+
+
+def test_pattern_attention_video720_workload():
+    cfg = configs.VIDEO720
+    say(f"[pattern workload] {cfg.name} (3 heads, 24 sampled tiles each)")
+    q, k, v = inputs.make_qkv(cfg, "cuda", H=3)
+    band = orc.band_halfwidth(parity.olayout(cfg), 0.25)
+    check_rows_attention(cfg.layout, q, k, v, np.array([PATTERNS], np.int32), band, 2,
+                         "bf16", sample_tiles=24)
+
+
+def test_pattern_attention_long_text_workload():
+    cfg = configs.VIDEO_LONG
+    say(f"[pattern workload] {cfg.name} (3 heads, 16 sampled tiles each)")
+    q, k, v = inputs.make_qkv(cfg, "cuda", H=3)
+    band = orc.band_halfwidth(parity.olayout(cfg), 0.25)
+    check_rows_attention(cfg.layout, q, k, v, np.array([PATTERNS], np.int32), band, 2,
+                         "bf16", sample_tiles=16)
+
+
+def test_rows_layout_matches_predicted_layout_bitwise():
+    """The predicted kept lists rewritten as padded rows give the same bytes
+    from rf_sparse_attn_rows as from rf_sparse_attn (full 720p, 8 heads)."""
+    cfg = configs.VIDEO720
+    s = 80
+    say(f"[rows vs predicted] {cfg.name} 8 heads s={s}")
+    q, k, v = inputs.make_qkv(cfg, "cuda", H=8)
+    plan = rf.Plan(cfg.layout)
+    z = plan.sizes
+    qp, qbar = rf.permute_means(plan, q)
+    kp, kbar = rf.permute_means(plan, k)
+    vt = rf.permute(plan, v, order=rf.TILES_T)
+    kept = rf.predict_mask(plan, qbar, kbar, s)
+    ref = rf.sparse_attn(plan, qp, kp, vt, kept, s)
+    kc = plan.keep(s)
+    width = kc["row_len_video"] + 3                 # extra -1 padding
+    rows = torch.full((1, 8, z["n_tiles"], width), -1, dtype=torch.int32, device="cuda")
+    rows[:, :, :, :kc["row_len_video"]] = kept.view(1, 8, z["nb"], kc["row_len_video"])
+    got = rf.sparse_attn_rows(plan, qp, kp, vt, rows)
+    torch.cuda.synchronize()
+    assert torch.equal(ref, got)
+    plan.close()
+
+
+@pytest.mark.parametrize("wt", [1, 2], ids=["bs64", "bs128"])
+def test_empty_and_short_rows(wt):
+    """An all -1 row gives zeros; a one-tile row attends to that tile only."""
+    lay = dict(T=2 * wt, H=8, W=16, wt=wt, wh=8, ww=8, n_text=0, permute=1, sink=0)
+    say(f"[rows] empty and one-tile rows, bs={64 * wt}")
+    plan = rf.Plan(lay)
+    z = plan.sizes
+    assert z["n_tiles"] == 4
+    bs = z["bs"]
+    olay = parity.olayout(lay)
+    for dt in (torch.bfloat16, torch.float32):
+        q, k, v = (_iid((1, 1, z["L"], 128), s, dt) for s in (7, 8, 9))
+        qp, kp = rf.permute(plan, q), rf.permute(plan, k)
+        vt = rf.permute(plan, v, order=rf.TILES_T)
+        rows = torch.tensor([[[[-1, -1, -1], [2, -1, -1], [0, 1, 3], [1, 3, -1]]]],
+                            dtype=torch.int32, device="cuda")
+        op = rf.sparse_attn_rows(plan, qp, kp, vt, rows)
+        torch.cuda.synchronize()
+        Lp = z["Lp"]
+        got = parity.values(op)[0, 0]
+        assert np.all(got[:bs] == 0)
+        want = orc.sparse_attention(parity.values(qp[:, :, :Lp]), parity.values(kp[:, :, :Lp]),
+                                    orc.permute(parity.values(v), olay),
+                                    [[[np.array([0]), np.array([2]), np.array([0, 1, 3]),
+                                       np.array([1, 3])]]], olay,
+                                    query_tiles={(0, 0): [1, 2, 3]})
+        parity.check_attention(got[:Lp], want[0, 0], orc.slot_valid(olay),
+                               "bf16" if dt == torch.bfloat16 else "f32")
+    plan.close()
+
+
+def test_unknown_pattern_gives_empty_video_rows():
+    lay = dict(T=3, H=13, W=21, wt=2, wh=8, ww=8, n_text=77, permute=1, sink=0)
+    say("[pattern] unknown pattern value")
+    plan = rf.Plan(lay)
+    z = plan.sizes
+    rows = rf.pattern_mask(plan, torch.tensor([[7, -1]], dtype=torch.int32, device="cuda"), 3, 2)
+    r = rows.cpu().numpy()
+    assert np.all(r[:, :, :z["nb"]] == -1)
+    for i in range(z["nb"], z["n_tiles"]):
+        assert r[0, 0, i, :z["n_tiles"]].tolist() == list(range(z["n_tiles"]))
+    plan.close()
+
+
+def test_recall_on_pattern_rows():
+    cfg = configs.VIDEO_LONG
+    say(f"[recall rows] {cfg.name} (3 heads)")
+    q, k, _ = inputs.make_qkv(cfg, "cuda", H=3)
+    lay = parity.olayout(cfg)
+    z = orc.sizes(lay)
+    plan = rf.Plan(cfg.layout)
+    qp, kp = rf.permute(plan, q), rf.permute(plan, k)
+    band = orc.band_halfwidth(lay, 0.25)
+    hp = np.array([PATTERNS], np.int32)
+    rows = rf.pattern_mask(plan, torch.tensor(hp, device="cuda"), band, 2)
+    samples = [0, 300, z["nb"] - 1, z["nb"]]
+    rec = rf.attention_recall_rows(plan, qp, kp, rows,
+                                   torch.tensor(samples, dtype=torch.int32, device="cuda"))
+    got = rec.cpu().numpy()
+    want_rows = orc.pattern_mask(lay, hp, band, 2)
+    Lp = z["Lp"]
+    for h in range(3):
+        want = orc.attention_recall(parity.values(qp[:, h:h + 1, :Lp]),
+                                    parity.values(kp[:, h:h + 1, :Lp]),
+                                    [[want_rows[0][h]]], lay, {(0, 0): samples})
+        for si, t in enumerate(samples):
+            w, g = want[(0, 0, t)], got[0, h, si]
+            assert np.array_equal(np.isnan(w), np.isnan(g))
+            m = ~np.isnan(w)
+            assert np.abs(g[m] - w[m]).max() <= 1e-4, f"h{h} tile {t}"
+    plan.close()
+
+
+# ------------------------------------------------------------------ ARM
+
+def check_arm(lay_dict, q, k, band, tau, strides, alpha=0.9, heads=None):
+    """GPU ARM recall for every pattern on both samples against the oracle,
+    then the decision.  q, k: raster device tensors."""
+    lay = parity.olayout(lay_dict)
+    plan = rf.Plan(lay_dict)
+    qp, kp = rf.permute(plan, q), rf.permute(plan, k)
+    qr, kr = parity.values(q), parity.values(k)
+    worst = 0.0
+    out = {}
+    for local, stride in zip((True, False), strides):
+        toks = orc.arm_samples(lay, local, stride)
+        for p in PATTERNS:
+            g = rf.arm_recall(plan, qp, kp, local, stride, p, band, tau).cpu().numpy()
+            assert g.shape[-1] == len(toks)
+            w = orc.arm_recall(qr, kr, lay, p, band, tau, toks)
+            err = np.abs(g - w).max()
+            worst = max(worst, err)
+            assert err <= 2e-5, f"ARM recall local={local} pattern={p}: {err:.3e}"
+            out[(local, p)] = (g, w)
+    loc_g, loc_w = out[(True, orc.TEMPORAL)]
+    glo_g, glo_w = out[(False, orc.SPATIAL)]
+    pat, mean = rf.arm_classify(torch.tensor(loc_g, device="cuda"),
+                                torch.tensor(glo_g, device="cuda"), alpha)
+    pat, mean = pat.cpu().numpy(), mean.cpu().numpy()
+    want_pat = orc.arm_classify(loc_w, glo_w, alpha)
+    bR, eR = loc_w.mean(axis=-1), glo_w.mean(axis=-1)
+    np.testing.assert_allclose(mean[..., 0], bR, atol=2e-5)
+    np.testing.assert_allclose(mean[..., 1], eR, atol=2e-5)
+    clear = (np.abs(bR - alpha) > 1e-4) & ((bR >= alpha) | (np.abs(eR - alpha) > 1e-4))
+    assert np.array_equal(pat[clear], want_pat[clear])
+    # the kernel's own decision on its own means is exact
+    exact = np.where(mean[..., 0] >= np.float32(alpha), orc.TEMPORAL,
+                     np.where(mean[..., 1] >= np.float32(alpha), orc.SPATIAL, orc.TEXTURAL))
+    assert np.array_equal(pat, exact)
+    say(f"  ARM recall max_abs={worst:.3e}; patterns {pat.ravel().tolist()}; "
+        f"bR={np.round(bR.ravel(), 3).tolist()} eR={np.round(eR.ravel(), 3).tolist()}")
+    plan.close()
+    return pat, mean
+
+
+@pytest.mark.parametrize("case", EDGE[:5], ids=[c[0] for c in EDGE[:5]])
+def test_arm_edge_layouts(case):
+    name, lay, B, H, d, dt, bw, tau = case
+    say(f"[ARM edge] {name}")
+    L = rf.layout_sizes(lay)["L"]
+    q, k = (_iid((B, H, L, d), s, dt) for s in (51, 52))
+    check_arm(lay, q, k, orc.band_halfwidth(parity.olayout(lay), bw), tau, (1, 3))
+
+
+def test_arm_video720_workload():
+    cfg = configs.VIDEO720
+    say(f"[ARM workload] {cfg.name} (4 heads, local stride 4, global stride 64)")
+    q, k, _ = inputs.make_qkv(cfg, "cuda", H=4)
+    band = orc.band_halfwidth(parity.olayout(cfg), 0.25)
+    check_arm(cfg.layout, q, k, band, 2, (4, 64))
+
+
+def test_arm_classify_decisions():
+    """Planted recalls whose means are exact in binary: the order of the
+    tests and the >= comparison."""
+    loc = torch.tensor([[[1.0, 0.25], [0.5, 0.5], [0.5, 1.0], [0.25, 0.25]]], device="cuda")
+    glo = torch.tensor([[[0.25, 0.25], [1.0, 0.5], [1.0, 1.0], [0.5, 0.75]]], device="cuda")
+    pat, mean = rf.arm_classify(loc, glo, 0.75)
+    assert pat.cpu().tolist() == [[orc.TEXTURAL, orc.SPATIAL, orc.TEMPORAL, orc.TEXTURAL]]
+    assert mean.cpu().tolist() == [[[0.625, 0.25], [0.5, 0.75], [0.75, 1.0], [0.25, 0.625]]]
+
+
+def test_arm_to_attention_pipeline_video720():
+    """Classify 4 heads of the 720p workload, build their pattern rows and
+    attend; sampled tiles against the oracle on the oracle's own rows."""
+    cfg = configs.VIDEO720
+    say(f"[ARM pipeline] {cfg.name} (4 heads)")
+    q, k, v = inputs.make_qkv(cfg, "cuda", H=4)
+    lay = parity.olayout(cfg)
+    band = orc.band_halfwidth(lay, 0.25)
+    plan = rf.Plan(cfg.layout)
+    qp, kp = rf.permute(plan, q), rf.permute(plan, k)
+    pat, _ = rf.arm_patterns(plan, qp, kp, band, 4, 64)
+    torch.cuda.synchronize()
+    hp = pat.cpu().numpy()
+    plan.close()
+    check_rows_attention(cfg.layout, q, k, v, hp, band, 2, "bf16", sample_tiles=12)
+
+
+def test_pattern_argument_errors():
+    plan = rf.Plan(configs.TINY.layout)
+    hp = torch.zeros((1, 2), dtype=torch.int32, device="cuda")
+    with pytest.raises(rf.RfError):
+        rf.pattern_mask(plan, hp, 1, 2, width=1)          # narrower than needed
+    z = plan.sizes
+    q = torch.zeros((1, 2, z["Lt"], 64), device="cuda")
+    with pytest.raises(rf.RfError):
+        rf.arm_recall(plan, q, q, True, 0, orc.TEMPORAL, 1)     # stride 0
+    with pytest.raises(rf.RfError):
+        rf.arm_recall(plan, q, q, True, 2, 5, 1)                # unknown pattern
+    rows = torch.zeros((1, 2, z["n_tiles"], z["n_tiles"] + 1), dtype=torch.int32, device="cuda")
+    with pytest.raises(rf.RfError):
+        rf.sparse_attn_rows(plan, q, q, q, rows)                # width > n_tiles
+    plan.close()
