@@ -423,6 +423,82 @@ def arm_classify(local_recall, global_recall, alpha: float) -> np.ndarray:
                     np.where(eR >= alpha, SPATIAL, TEXTURAL))
 
 
+E4M3_MAX = 448.0
+
+
+def e4m3(x) -> np.ndarray:
+    """Round to the nearest OCP e4m3 value, ties to even (reading R12).
+    Normal numbers |x| >= 2^-6 have 3 fraction bits, so the spacing is
+    2^(E - 3) for |x| in [2^E, 2^(E+1)); below 2^-6 the spacing is the
+    subnormal step 2^-9.  Values that round above 448 are not representable
+    and raise."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    with np.errstate(divide="ignore"):
+        E = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    step = np.exp2(np.maximum(E, -6.0) - 3.0)
+    r = np.round(a / step) * step          # np.round: half to even
+    if np.any(r > E4M3_MAX):
+        raise ValueError("value outside the e4m3 range")
+    return np.copysign(r, x)
+
+
+def pow2_exponent(amax: float) -> int:
+    """Smallest integer e with amax <= 448 * 2^e; 0 for amax == 0 (R12)."""
+    amax = float(amax)
+    if amax == 0.0:
+        return 0
+    e = math.ceil(math.log2(amax / E4M3_MAX))
+    while amax > E4M3_MAX * 2.0 ** e:
+        e += 1
+    while amax <= E4M3_MAX * 2.0 ** (e - 1):
+        e -= 1
+    return e
+
+
+def quantize_tiles(xp, lay: Layout):
+    """Per-(b, h, tile) power-of-two scaled e4m3 of a permuted tensor
+    [B, H, Lp, d] (reading R12).  Returns (dequantized values, fp64, same
+    shape; exponents [B, H, n_tiles])."""
+    z = sizes(lay)
+    bs = z["bs"]
+    B, H, Lp, d = xp.shape
+    out = np.empty(xp.shape, dtype=np.float64)
+    ex = np.zeros((B, H, z["n_tiles"]), dtype=np.int64)
+    for b in range(B):
+        for h in range(H):
+            for t in range(z["n_tiles"]):
+                rows = slice(t * bs, min((t + 1) * bs, Lp))
+                x = xp[b, h, rows].astype(np.float64)
+                e = pow2_exponent(np.abs(x).max() if x.size else 0.0)
+                ex[b, h, t] = e
+                out[b, h, rows] = e4m3(x * 2.0 ** -e) * 2.0 ** e
+    return out, ex
+
+
+def quantize_channels(xp):
+    """Per-(b, h, feature) power-of-two scaled e4m3 over all slots of a
+    permuted tensor [B, H, Lp, d] (reading R12).  Returns (dequantized
+    values, exponents [B, H, d])."""
+    B, H, _, d = xp.shape
+    x = xp.astype(np.float64)
+    amax = np.abs(x).max(axis=2)
+    ex = np.vectorize(pow2_exponent, otypes=[np.int64])(amax)
+    scale = np.exp2(ex)[:, :, None, :]
+    return e4m3(x / scale) * scale, ex
+
+
+def sparse_attention_fp8(qp, kp, vp, kept, lay: Layout, scale=None,
+                         query_tiles=None):
+    """Block-sparse attention over e4m3-quantized Q, K (per tile) and V (per
+    feature), reading R12: `sparse_attention` on the dequantized values."""
+    q8, _ = quantize_tiles(qp, lay)
+    k8, _ = quantize_tiles(kp, lay)
+    v8, _ = quantize_channels(vp)
+    return sparse_attention(q8, k8, v8, kept, lay, scale=scale,
+                            query_tiles=query_tiles)
+
+
 def run(q, k, v, lay: Layout, sparsity_pct: int, query_tiles=None):
     """The whole path on raster inputs [B, H, N + n_text, d] (any float
     dtype; computed in fp64): permute, pool, predict, attend, unpermute."""

@@ -713,3 +713,104 @@ def test_arm_classification_order():
     glo = np.array([[[0.25, 0.25], [1.0, 0.5], [1.0, 1.0], [0.5, 0.75]]])
     got = orc.arm_classify(loc, glo, a)
     assert got.tolist() == [[orc.TEXTURAL, orc.SPATIAL, orc.TEMPORAL, orc.TEXTURAL]]
+
+
+# ------------------------------------------------------------------ FP8
+
+def _e4m3_decode(c):
+    """Value of an e4m3 bit pattern from the format's fields."""
+    s = -1.0 if c & 0x80 else 1.0
+    e, m = (c >> 3) & 15, c & 7
+    if e == 15 and m == 7:
+        return math.nan
+    return s * (m / 8 * 2.0 ** -6 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7))
+
+
+def test_e4m3_grid_from_the_format_fields():
+    """Every finite code is a fixed point; 448 is the largest; the subnormal
+    step is 2^-9; 254 finite codes give 253 distinct values (+-0 equal)."""
+    vals = [_e4m3_decode(c) for c in range(256)]
+    finite = np.array([v for v in vals if not math.isnan(v)])
+    assert len(finite) == 254 and len(set(finite.tolist())) == 253
+    np.testing.assert_array_equal(orc.e4m3(finite), finite)
+    assert finite.max() == 448.0 and sorted(set(np.abs(finite)))[1] == 2.0 ** -9
+
+
+def test_e4m3_rounds_to_nearest_even_like_torch():
+    """Midpoints go to the even code, neighbours of a midpoint to the
+    nearer value; the same as torch's CPU float8_e4m3fn conversion (a
+    library routine) on the midpoints, their float32 neighbours and random
+    values."""
+    import torch
+    pos = sorted(set(abs(v) for v in (_e4m3_decode(c) for c in range(128))
+                     if not math.isnan(v)))
+    x = []
+    for lo, hi in zip(pos[:-1], pos[1:]):
+        mid = np.float32((lo + hi) / 2)
+        x += [lo, mid, np.nextafter(mid, np.float32(0)), np.nextafter(mid, np.float32(1e9))]
+    x = np.array(x + list(_rng(71).standard_normal(5000) * 40), np.float32)
+    x = np.concatenate([x, -x])
+    x = x[np.abs(x) <= 464]
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(orc.e4m3(x), want)
+    # ties by hand: 1 + 1/16 lies between 1 and 1.125 -> 1 (even mantissa 0);
+    # 1 + 3/16 between 1.125 and 1.25 -> 1.25 (mantissa 2)
+    assert orc.e4m3(1 + 1 / 16) == 1.0 and orc.e4m3(1 + 3 / 16) == 1.25
+    with pytest.raises(ValueError):
+        orc.e4m3(465.0)
+
+
+def test_pow2_exponent_closed_forms():
+    assert orc.pow2_exponent(0.0) == 0
+    assert orc.pow2_exponent(448.0) == 0 and orc.pow2_exponent(448.5) == 1
+    assert orc.pow2_exponent(224.0) == -1 and orc.pow2_exponent(224.5) == 0
+    assert orc.pow2_exponent(3.5) == -7 and orc.pow2_exponent(3.75) == -6
+    for a in _rng(73).uniform(1e-6, 1e6, 200):
+        e = orc.pow2_exponent(a)
+        assert 224.0 < a / 2.0 ** e <= 448.0
+
+
+def test_quantize_tiles_and_channels():
+    """Scaled codes reach into (224, 448] in every nonzero tile; the
+    dequantized error is within half a step (2^-4 relative above the
+    subnormal range); pad slots stay 0."""
+    lay = orc.Layout(3, 5, 7, 2, 2, 4, n_text=9)
+    z = orc.sizes(lay)
+    r = _rng(79)
+    xp = orc.permute(r.standard_normal((1, 2, z["L"], 8)) * 3, lay)
+    q, ex = orc.quantize_tiles(xp, lay)
+    bs = z["bs"]
+    for t in range(z["n_tiles"]):
+        rows = slice(t * bs, min((t + 1) * bs, z["Lp"]))
+        for h in range(2):
+            x = xp[0, h, rows]
+            amax = np.abs(x).max()
+            assert 224 < amax / 2.0 ** ex[0, h, t] <= 448
+            err = np.abs(q[0, h, rows] - x)
+            tol = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** (ex[0, h, t] - 10))
+            assert np.all(err <= tol + 1e-300)
+    assert np.all(q[:, :, ~orc.slot_valid(lay)] == 0)
+    v, evx = orc.quantize_channels(xp)
+    amax = np.abs(xp).max(axis=2)
+    assert np.all((amax / 2.0 ** evx > 224) & (amax / 2.0 ** evx <= 448))
+
+
+def test_fp8_attention_is_exact_on_representable_inputs():
+    """Inputs in {-2, ..., 2}: every tile and feature max is 2, the scale is
+    2^-7 and 2 * 2^7 = 256 is a code, so quantization is the identity and
+    the fp8 attention equals the plain one."""
+    lay = orc.Layout(2, 6, 6, 1, 4, 4, n_text=5)
+    z = orc.sizes(lay)
+    r = _rng(83)
+    x = [r.integers(-2, 3, size=(1, 1, z["L"], 8)).astype(np.float64) for _ in range(3)]
+    for t in x:
+        t[..., 0, :] = 2.0              # make sure every feature reaches 2
+    qp, kp, vp = (orc.permute(t, lay) for t in x)
+    # every query/key tile must reach 2 too
+    for t in range(z["n_tiles"]):
+        qp[0, 0, t * z["bs"], 0] = 2.0
+        kp[0, 0, t * z["bs"], 0] = 2.0
+    kept, _ = orc.predict_mask(orc.block_means(qp, lay), orc.block_means(kp, lay), lay, 50)
+    a = orc.sparse_attention(qp, kp, vp, kept, lay)
+    b = orc.sparse_attention_fp8(qp, kp, vp, kept, lay)
+    np.testing.assert_array_equal(a, b)
