@@ -30,6 +30,7 @@ if ROOT not in sys.path:
 METRIC = "block-sparse attn TFLOP/s, ms/call @75.6k tok 80% sparse, MFMA util"
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3
+PEAK_FP8_TFLOPS = 5000.0        # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0
 ATTN_SRC = os.path.join(ROOT, "image_diffusion_dits_amd", "csrc", "attn.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
@@ -60,6 +61,9 @@ def parse():
                          "(first 10%% of steps dense) on the 720p workload")
     ap.add_argument("--refresh", type=int, default=1,
                     help="with --schedule: predict the mask every R sparse steps")
+    ap.add_argument("--fp8", action="store_true",
+                    help="run the attention on OCP e4m3 operands (the quantization "
+                         "of Q, K and V is a stage of the timed step)")
     ap.add_argument("--patterns", action="store_true",
                     help="instead of the step benchmark, time the v1 head-pattern "
                          "path on the 720p workload: ARM recall and decision, "
@@ -260,11 +264,12 @@ def stored_traffic(workload, per_launch_flop):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, q, k, v, sparsity, n_tiles_sample, exec_flop_total):
+def cpu_baseline(cfg, q, k, v, sparsity, n_tiles_sample, exec_flop_total, fp8=False):
     """Time the fp64 oracle on one head: the whole of permute, means, mask
-    and unpermute, plus attention on a sample of query tiles; extrapolate to
-    all heads and tiles (heads are independent and every video row keeps the
-    same number of tiles)."""
+    (with fp8, the e4m3 quantization of Q, K, V too) and unpermute, plus
+    attention on a sample of query tiles; extrapolate to all heads and tiles
+    (heads are independent and every video row keeps the same number of
+    tiles)."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -279,6 +284,10 @@ def cpu_baseline(cfg, q, k, v, sparsity, n_tiles_sample, exec_flop_total):
     qp, kp, vp = (orc.permute(x, lay) for x in (qh, kh, vh))
     qbar, kbar = orc.block_means(qp, lay), orc.block_means(kp, lay)
     kept, _ = orc.predict_mask(qbar, kbar, lay, sparsity)
+    if fp8:      # the oracle's fp8 attention is attention over these values
+        qp, _ = orc.quantize_tiles(qp, lay)
+        kp, _ = orc.quantize_tiles(kp, lay)
+        vp, _ = orc.quantize_channels(vp)
     t1 = time.perf_counter()
     rng = np.random.default_rng(0)
     tiles = sorted(rng.choice(z["nb"], size=min(n_tiles_sample, z["nb"]),
@@ -345,25 +354,45 @@ def main():
     kept = torch.empty(B, H, kc["nnz_per_head"], dtype=torch.int32, device=dev)
     op = torch.empty_like(qp)
     o = torch.empty_like(q)
+    if a.fp8:
+        q8 = torch.empty(qp.shape, dtype=torch.uint8, device=dev)
+        k8 = torch.empty_like(q8)
+        v8 = torch.empty(vt.shape, dtype=torch.uint8, device=dev)
+        qs = torch.empty(B, H, z["n_tiles"], dtype=torch.float32, device=dev)
+        ks = torch.empty_like(qs)
+        vs = torch.empty(B, H, d, dtype=torch.float32, device=dev)
 
-    stages = ["permute_means_qk", "permute_v", "predict_mask", "sparse_attn", "unpermute"]
+    stages = ["permute_means_qk", "permute_v", "predict_mask"]
+    stages += ["quantize_fp8"] if a.fp8 else []
+    stages += ["sparse_attn", "unpermute"]
+    n_ev = len(stages) + 1
 
     def step(ev=None):
-        def mark(i):
+        marks = iter(range(n_ev))
+
+        def mark():
+            i = next(marks)
             if ev is not None:
                 ev[i].record()
-        mark(0)
+        mark()
         rf.permute_means(plan, q, out=qp, xbar=qbar)
         rf.permute_means(plan, k, out=kp, xbar=kbar)
-        mark(1)
+        mark()
         rf.permute(plan, v, order=rf.TILES_T, out=vt)
-        mark(2)
+        mark()
         rf.predict_mask(plan, qbar, kbar, s, kept=kept)
-        mark(3)
-        rf.sparse_attn(plan, qp, kp, vt, kept, s, out=op)
-        mark(4)
+        mark()
+        if a.fp8:
+            rf.quantize_fp8(plan, qp, out=q8, scale=qs)
+            rf.quantize_fp8(plan, kp, out=k8, scale=ks)
+            rf.quantize_fp8(plan, vt, order=rf.TILES_T, out=v8, scale=vs)
+            mark()
+            rf.sparse_attn_fp8(plan, q8, qs, k8, ks, v8, vs, kept, s, out=op)
+        else:
+            rf.sparse_attn(plan, qp, kp, vt, kept, s, out=op)
+        mark()
         rf.unpermute(plan, op, out=o)
-        mark(5)
+        mark()
 
     for _ in range(a.warmup):
         step()
@@ -379,7 +408,7 @@ def main():
 
     # Timed region 2: the same steps with HIP events between stages (all
     # kernels run on torch's current stream, which the events are recorded on).
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
            for _ in range(a.steps)]
     torch.cuda.synchronize()
     for i in range(a.steps):
@@ -387,7 +416,7 @@ def main():
     torch.cuda.synchronize()
     stage_ms = {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / a.steps
                 for j, name in enumerate(stages)}
-    ev_step_ms = sum(e[0].elapsed_time(e[5]) for e in evs) / a.steps
+    ev_step_ms = sum(e[0].elapsed_time(e[n_ev - 1]) for e in evs) / a.steps
 
     pairs = kc["nnz_per_head"] * B * H
     exec_flop = 4.0 * d * bs * bs * pairs
@@ -395,10 +424,13 @@ def main():
     dense_flop = 4.0 * B * H * L * L * d
     attn_s = stage_ms["sparse_attn"] / 1e3
     ms_step = wall * 1e3
-    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    if a.fp8:
+        peak = PEAK_FP8_TFLOPS
+    else:
+        peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
     attn_tflops = exec_flop / attn_s / 1e12
     workload = cfg.name + ("" if cfg.permute else "-raster")
-    traffic = stored_traffic(workload, exec_flop)
+    traffic = None if a.fp8 else stored_traffic(workload, exec_flop)
     aux_ms = sum(stage_ms[n] for n in stages if n != "sparse_attn")
     esize = 2 if cfg.dtype == "bf16" else 4
     perm_bytes = B * H * (z["L"] + z["Lt"]) * d * esize   # one tensor
@@ -415,7 +447,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": cfg.dtype,
+        "dtype": "fp8" if a.fp8 else cfg.dtype,
         "data": "synthetic",
         "config": {
             "workload": workload, "batch": B, "heads": H, "head_dim": d,
@@ -439,7 +471,8 @@ def main():
             "unpermute": round(unperm_bytes / (stage_ms["unpermute"] / 1e3) / 1e9, 1),
         },
         "roofline": {
-            "kernel": "attn_bf16_pp_kernel" if cfg.dtype == "bf16" else "attn_f32_kernel",
+            "kernel": ("attn_fp8_pp_kernel" if a.fp8 else
+                       "attn_bf16_pp_kernel" if cfg.dtype == "bf16" else "attn_f32_kernel"),
             "bound": "mfma",
             "achieved": round(attn_tflops, 2),
             "peak": peak,
@@ -448,6 +481,17 @@ def main():
             "traffic": traffic,
         },
     }
+    if a.fp8:
+        # Cost of the e4m3 operands: the same step's output against the bf16
+        # attention on the same permuted tensors.
+        ref = rf.sparse_attn(plan, qp, kp, vt, kept, s)
+        torch.cuda.synchronize()
+        diff = (op.float() - ref.float()).abs()
+        rec["fp8_vs_bf16_attention"] = {"max_abs": round(float(diff.max()), 5),
+                                        "mean_abs": round(float(diff.mean()), 6)}
+        rec["config"]["operands"] = ("e4m3: Q, K per-tile and V per-feature "
+                                     "power-of-two scales; softmax weights e4m3")
+        del ref, diff
     if a.copy_probe:
         # torch.neg reads and writes exactly n*2 bytes: a plain copy kernel
         # whose HBM counters calibrate the attention kernel's.
@@ -459,7 +503,7 @@ def main():
         torch.cuda.synchronize()
         rec["copy_probe_bytes"] = {"read": 2 * n, "write": 2 * n}
     if not a.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(cfg, q, k, v, s, a.cpu_tiles, exec_flop)
+        rec["cpu_baseline"] = cpu_baseline(cfg, q, k, v, s, a.cpu_tiles, exec_flop, a.fp8)
     print(json.dumps(rec), flush=True)
     plan.close()
     return 0

@@ -1,0 +1,357 @@
+// FP8 variant of the block-sparse attention forward (RainFusion2.0 page,
+// TL;DR: integration with quantization named as future work): QK^T and PV on
+// OCP e4m3 operands with v_mfma_f32_32x32x64_f8f6f4, fp32 accumulation and
+// softmax, bf16 output.  Operands come from rf_quantize_fp8: Q and K with one
+// power-of-two scale per tile, V^T tiles with one per feature.
+//
+// The structure is the bf16 ping-pong kernel's (two groups of four waves per
+// 128-slot query tile, one phase apart: MFMA phase PV(i-1) then S(i), VALU
+// phase softmax(i) while the group's next K and V^T tiles are copied into
+// LDS).  What changes with 8-bit operands:
+//   * one MFMA reduces 64 features (or keys): 8 MFMAs for S and 8 for PV per
+//     tile and wave, each fed 32 bytes per lane (two 16-byte LDS reads);
+//   * P^T must reach the PV MFMA straight from the S^T accumulators.  Lane
+//     group g of S block kb holds MFMA rows 8a + 4g + b, so K rows are
+//     copied into LDS permuted: LDS row 32 kb + x holds key
+//       pi(kb, x) = 64 (kb/2) + 32 ((x/4) % 2) + 16 (kb % 2) + 4 (x/8) + x % 4,
+//     and register r of block kb in lane group g is key
+//       64 (kb/2) + 32 g + 16 (kb % 2) + r.
+//     The 32 weights of blocks 2s and 2s + 1 in lane group g are then keys
+//     64 s + 32 g .. +32 in order, which is exactly the 32-byte V^T run the
+//     same lane group reads for k-step s;
+//   * the row sum of the e4m3 weights comes from two more MFMAs with an
+//     all-ones A operand, so the normalisation uses the weights the PV
+//     product used and the vector ALU does not convert them back;
+//   * logits are dot(q8, k8) * scale * 2^(eq + ek) (the key tile's scale
+//     enters the exp2 multiplier), and the feature scales of V multiply the
+//     output once at the end.
+// Weights are exp2(l - m) <= 2^8 under the lazy rescale (threshold 8), inside
+// the e4m3 range (448).
+#include "rf_internal.h"
+#include "tile_common.h"
+
+namespace {
+
+using namespace rf_tile;
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int D = 128;
+constexpr int BS = 128;
+constexpr int kGroupWaves = 4;
+constexpr int kThreads = 2 * kGroupWaves * 64;
+constexpr int kRowBytes = 128;                  // K row (D fp8) and V^T row (BS fp8)
+constexpr int kTileBytes = BS * D;              // 16 KB
+constexpr int kCopies = kTileBytes / 16 / (kGroupWaves * 64);   // 4 per thread
+static_assert(kCopies == 4, "copy split");
+
+__device__ inline f32x16 mma(const i32x8& a, const i32x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ inline i32x8 lds32(const uint8_t* row, int c0, int swz) {
+  const i32x4 lo = *reinterpret_cast<const i32x4*>(row + ((c0) ^ swz) * 16);
+  const i32x4 hi = *reinterpret_cast<const i32x4*>(row + ((c0 + 1) ^ swz) * 16);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ inline int pack4(float a, float b, float c, float d) {
+  int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
+}
+
+__global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
+    const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
+    const uint8_t* __restrict__ k8, const float* __restrict__ k_scale,
+    const uint8_t* __restrict__ v8, const float* __restrict__ v_scale,
+    const int32_t* __restrict__ kept, __bf16* __restrict__ op,
+    const uint32_t* __restrict__ tile_bits, const int32_t* __restrict__ tile_count,
+    int64_t Lt, int32_t BH, int32_t nb, int32_t n_tt, int32_t row_len_video, int64_t nnz,
+    float scale_log2) {
+  constexpr int kWaitVm0 = 0x0F70;     // s_waitcnt vmcnt(0)
+  // K and V^T tiles of group 0, then of group 1; reused for the merge.
+  __shared__ __align__(16) uint8_t lds[4 * kTileBytes];
+  __shared__ float m_buf[kGroupWaves * 64], l_buf[kGroupWaves * 64];
+
+  const int32_t n_tiles = nb + n_tt;
+  const TileJob job = job_of(blockIdx.x, BH, nb, n_tt);
+  const int64_t bh = job.bh;
+  const int32_t qtile = job.tile;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  const int grp = wave / kGroupWaves;
+  const int qw = wave % kGroupWaves;
+  const int lane = threadIdx.x % 64;
+  const int li = lane % 32, g = lane / 32;
+  uint8_t* const ks = lds + (2 * grp) * kTileBytes;
+  uint8_t* const vs = lds + (2 * grp + 1) * kTileBytes;
+
+  const char* kh = reinterpret_cast<const char*>(k8 + bh * Lt * D);
+  const char* vh = reinterpret_cast<const char*>(v8 + bh * int64_t(n_tiles) * D * BS);
+  const float* ksc = k_scale + bh * n_tiles;
+  const rf::RowRef rr = rf::row_ref(kept + bh * nnz, qtile, nb, row_len_video, n_tiles);
+  const __attribute__((address_space(4))) int32_t* row =
+      (const __attribute__((address_space(4))) int32_t*)(kept + bh * nnz + rr.offset);
+  const int32_t row_len = rr.len;
+  const int32_t n_grp = (row_len + 1) / 2;
+  auto tile_of = [&](int32_t i) -> int32_t {
+    const int32_t j = 2 * i + grp;
+    const int32_t kt = row[max(min(j, row_len - 1), 0)];
+    return (j < row_len && kt >= 0 && kt < n_tiles) ? kt : -1;
+  };
+
+  // Q operand (B of S^T = K Q^T): lane (li, g) holds q[li][64m + 32g .. +32].
+  const int64_t qrow = int64_t(qtile) * BS + qw * 32 + li;
+  i32x8 qf[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+    qf[m] = *reinterpret_cast<const i32x8*>(q8 + (bh * Lt + qrow) * D + 64 * m + 32 * g);
+  const float c_q = scale_log2 * q_scale[bh * n_tiles + qtile];
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+  f32x16 lsum = {};                     // every register: the row sum
+  float m_run = -INFINITY;
+  f32x16 s[BS / 32];
+  i32x8 pb[2];
+  const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                      0x38383838, 0x38383838, 0x38383838, 0x38383838};   // e4m3 1.0
+
+  // Copies.  V^T rows land in order; K rows land permuted by pi: copy u fills
+  // LDS rows 32u .. 32u + 31 (block kb = u), whose keys are those of copy 0
+  // shifted by 64 (u/2) + 16 (u%2).  The swizzle of row 32u + x equals that
+  // of row x.
+  const int qlin = qw * 64 + lane;
+  const int xr = qlin / 8, pc = qlin % 8;
+  const int key0 = 32 * ((xr / 4) % 2) + 4 * (xr / 8) + xr % 4;
+  const uint32_t koff = uint32_t(key0 * kRowBytes + (pc ^ swz_rows<kRowBytes>(xr)) * 16);
+  const uint32_t ksoff[kCopies] = {0u, 16u * kRowBytes, 64u * kRowBytes, 80u * kRowBytes};
+  const uint32_t voff = dma_offset<kRowBytes, kRowBytes, kGroupWaves>(qw, lane);
+  auto copy_k = [&](int32_t kt) {
+    dma_tile_perm<kCopies, kGroupWaves>(kh + int64_t(max(kt, 0)) * kTileBytes, kTileBytes,
+                                        ks, koff, qw, ksoff);
+  };
+  auto copy_v = [&](int32_t kt) {
+    dma_tile<kCopies, kGroupWaves>(vh + int64_t(max(kt, 0)) * kTileBytes, kTileBytes, vs,
+                                   voff, qw);
+  };
+  const int rswz = swz_rows<kRowBytes>(li);     // rows 32 kb + li and 32 db + li
+
+  constexpr int kAhead = 4;                     // MFMAs whose operands are read ahead
+  auto pipeline_reads = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);    // DS reads
+#pragma unroll
+    for (int j = 0; j < 8 - kAhead; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);           // DS reads
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
+  };
+
+  auto mfma_phase = [&](int32_t i) {
+    if (i >= 1) {
+      // O^T[db] += V^T[db rows, keys 64s .. +64] P^T(i-1), k-steps s = 0, 1.
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+          o[db] = mma(lds32(vs + (db * 32 + li) * kRowBytes, 4 * st + 2 * g, rswz), pb[st], o[db]);
+      pipeline_reads();
+      lsum = mma(ones, pb[0], lsum);
+      lsum = mma(ones, pb[1], lsum);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (i < n_grp) {
+#pragma unroll
+      for (int kb = 0; kb < BS / 32; ++kb) {
+        s[kb] = f32x16{};
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+          s[kb] = mma(lds32(ks + (kb * 32 + li) * kRowBytes, 4 * m + 2 * g, rswz), qf[m], s[kb]);
+      }
+      pipeline_reads();
+    }
+  };
+
+  auto valu_phase = [&](int32_t i) {
+    if (i < 0 || i >= n_grp) return;
+    const int32_t kt = tile_of(i);
+    if (i + 1 < n_grp) copy_k(tile_of(i + 1));
+    copy_v(kt);
+    const int32_t tcount = kt >= 0 ? tile_count[kt] : 0;
+    if (tcount != BS) {
+      // Register r of block kb in lane group g is key 64(kb/2) + 32g +
+      // 16(kb%2) + r: validity word 2(kb/2) + g, bit 16(kb%2) + r.
+#pragma unroll
+      for (int kb = 0; kb < BS / 32; ++kb) {
+        const uint32_t bits =
+            (kt >= 0 ? tile_bits[kt * 4 + 2 * (kb / 2) + g] : 0u) >> (16 * (kb % 2));
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (!((bits >> r) & 1u)) s[kb][r] = -INFINITY;
+      }
+    }
+    const float c = c_q * (kt >= 0 ? ksc[kt] : 1.f);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < BS / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    {
+      const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx),
+                                                       __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+    }
+    const float mt = mx * c;
+    if (__ballot(mt > m_run + 8.f) != 0) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      lsum[0] *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+    }
+    const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int kb = 2 * st + e / 4, r0 = 4 * (e % 4);
+        float p[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          p[j] = __builtin_amdgcn_exp2f(fmaf(s[kb][r0 + j], c, neg_m));
+        pb[st][e] = pack4(p[0], p[1], p[2], p[3]);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);   // the copies have landed
+  };
+
+  if (n_grp > 0) copy_k(tile_of(0));
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __builtin_amdgcn_s_barrier();
+  if (grp == 0) {
+    for (int32_t i = 0; i <= n_grp; ++i) {
+      mfma_phase(i);
+      __builtin_amdgcn_s_barrier();
+      valu_phase(i);
+      __builtin_amdgcn_s_barrier();
+    }
+  } else {
+    for (int32_t i = 0; i <= n_grp; ++i) {
+      valu_phase(i - 1);
+      __builtin_amdgcn_s_barrier();
+      mfma_phase(i);
+      __builtin_amdgcn_s_barrier();
+    }
+  }
+
+  // Merge: group 1 publishes O (register quads), m and l; group 0 combines,
+  // applies the feature scales of V and stores.
+  float4* ob = reinterpret_cast<float4*>(lds);
+  constexpr int kQuads = D / 32 * 4;
+  const float l_run = lsum[0];
+  if (grp == 1) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        ob[((qw * kQuads + db * 4 + a) * 64) + lane] =
+            make_float4(o[db][4 * a], o[db][4 * a + 1], o[db][4 * a + 2], o[db][4 * a + 3]);
+    m_buf[qw * 64 + lane] = m_run;
+    l_buf[qw * 64 + lane] = l_run;
+  }
+  __syncthreads();
+  if (grp == 1) return;
+  const float m_b = m_buf[qw * 64 + lane], l_b = l_buf[qw * 64 + lane];
+  const float m_t = fmaxf(m_run, m_b);
+  const float fa = m_t == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_t);
+  const float fb = m_t == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_b - m_t);
+  const float l_tot = l_run * fa + l_b * fb;   // both lane groups hold the full sum
+  const int qs = qw * 32 + li;
+  const bool qvalid = (tile_bits[qtile * 4 + qs / 32] >> (qs % 32)) & 1u;
+  const float inv = (qvalid && l_tot > 0.f) ? 1.f / l_tot : 0.f;
+  const float ca = fa * inv, cb = fb * inv;
+  // Lane (li, g) holds O^T[dd = db*32 + 8a + 4g + b][query li].
+  __bf16* dst = op + (bh * Lt + qrow) * D + 4 * g;
+  const float* vsc = v_scale + bh * D + 4 * g;
+  typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+  typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const float4 x = ob[((qw * kQuads + db * 4 + a) * 64) + lane];
+      const float4 w = *reinterpret_cast<const float4*>(vsc + db * 32 + 8 * a);
+      const f32x4 f = {(o[db][4 * a] * ca + x.x * cb) * w.x,
+                       (o[db][4 * a + 1] * ca + x.y * cb) * w.y,
+                       (o[db][4 * a + 2] * ca + x.z * cb) * w.z,
+                       (o[db][4 * a + 3] * ca + x.w * cb) * w.w};
+      *reinterpret_cast<bf16x4*>(dst + db * 32 + 8 * a) = __builtin_convertvector(f, bf16x4);
+    }
+  }
+}
+
+rf_status attn_fp8(const rf_plan* plan, const void* q8, const float* q_scale, const void* k8,
+                   const float* k_scale, const void* v8, const float* v_scale,
+                   const int32_t* kept, int32_t row_len_video, int64_t nnz, void* op,
+                   int32_t B, int32_t H, int32_t d, float scale, hipStream_t stream,
+                   const char* fn) {
+  rf_status st = rf::check_call(plan, B, H, d, RF_BF16, fn);
+  if (st != RF_OK) return st;
+  if (d != D || plan->sz.bs != BS)
+    return rf::fail(RF_ERR_UNSUPPORTED, "%s: the FP8 kernel needs d = %d and bs = %d", fn, D, BS);
+  if (!rf::aligned16(q8) || !rf::aligned16(k8) || !rf::aligned16(v8) ||
+      !rf::aligned16(kept) || !rf::aligned16(op) || !rf::aligned16(v_scale) ||
+      q_scale == nullptr || k_scale == nullptr ||
+      (reinterpret_cast<uintptr_t>(q_scale) & 3u) || (reinterpret_cast<uintptr_t>(k_scale) & 3u))
+    return rf::fail(RF_ERR_INVALID_ARG, "%s: null or misaligned buffer", fn);
+  if (!(scale > 0.f) || !(scale < 1e30f))
+    return rf::fail(RF_ERR_INVALID_ARG, "%s: scale must be positive and finite", fn);
+  const int BH = B * H;
+  if (int64_t(BH) * plan->sz.n_tiles >= (int64_t(1) << 31))
+    return rf::fail(RF_ERR_UNSUPPORTED, "%s: too many tiles", fn);
+  const int nb = plan->sz.nb, n_tt = plan->sz.n_text_tiles;
+  hipLaunchKernelGGL(attn_fp8_pp_kernel, dim3(BH * (nb + n_tt)), dim3(kThreads), 0, stream,
+                     static_cast<const uint8_t*>(q8), q_scale, static_cast<const uint8_t*>(k8),
+                     k_scale, static_cast<const uint8_t*>(v8), v_scale, kept,
+                     static_cast<__bf16*>(op), plan->tile_bits, plan->tile_count,
+                     plan->sz.Lt, BH, nb, n_tt, row_len_video, nnz,
+                     scale * 1.4426950408889634f);
+  return rf::check_launch(fn);
+}
+
+}  // namespace
+
+extern "C" rf_status rf_sparse_attn_fp8(const rf_plan* plan, const void* q8,
+                                        const float* q_scale, const void* k8,
+                                        const float* k_scale, const void* v8,
+                                        const float* v_scale, const int32_t* kept_idx,
+                                        int32_t sparsity_pct, void* op, int32_t B, int32_t H,
+                                        int32_t d, float scale, hipStream_t stream) {
+  if (plan == nullptr) return rf::fail(RF_ERR_INVALID_ARG, "rf_sparse_attn_fp8: null plan");
+  rf_keep kc;
+  rf_status st = rf_keep_count(&plan->lay, sparsity_pct, &kc);
+  if (st != RF_OK) return st;
+  return attn_fp8(plan, q8, q_scale, k8, k_scale, v8, v_scale, kept_idx, kc.row_len_video,
+                  kc.nnz_per_head, op, B, H, d, scale, stream, "rf_sparse_attn_fp8");
+}
+
+extern "C" rf_status rf_sparse_attn_fp8_rows(const rf_plan* plan, const void* q8,
+                                             const float* q_scale, const void* k8,
+                                             const float* k_scale, const void* v8,
+                                             const float* v_scale, const int32_t* kept_rows,
+                                             int32_t row_width, void* op, int32_t B,
+                                             int32_t H, int32_t d, float scale,
+                                             hipStream_t stream) {
+  if (plan == nullptr)
+    return rf::fail(RF_ERR_INVALID_ARG, "rf_sparse_attn_fp8_rows: null plan");
+  if (row_width < 1 || row_width > plan->sz.n_tiles)
+    return rf::fail(RF_ERR_INVALID_ARG, "rf_sparse_attn_fp8_rows: row_width %d outside [1, %d]",
+                    row_width, plan->sz.n_tiles);
+  return attn_fp8(plan, q8, q_scale, k8, k_scale, v8, v_scale, kept_rows, -row_width,
+                  int64_t(plan->sz.n_tiles) * row_width, op, B, H, d, scale, stream,
+                  "rf_sparse_attn_fp8_rows");
+}

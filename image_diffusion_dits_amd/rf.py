@@ -86,6 +86,12 @@ _SIGNATURES = {
                       _c_i32, _c_i32, _c_i32, _c_f32, ctypes.c_int, _vp, _vp],
     "rf_arm_classify": [_vp, _c_i32, _vp, _c_i32, _c_i32, _c_f32, _vp, _vp,
                         _vp],
+    "rf_quantize_fp8": [_vp, _vp, ctypes.c_int, _vp, _vp, _c_i32, _c_i32, _c_i32,
+                        ctypes.c_int, _vp],
+    "rf_sparse_attn_fp8": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _vp,
+                           _c_i32, _c_i32, _c_i32, _c_f32, _vp],
+    "rf_sparse_attn_fp8_rows": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i32,
+                                _vp, _c_i32, _c_i32, _c_i32, _c_f32, _vp],
 }
 
 _lib = None
@@ -444,6 +450,64 @@ def arm_patterns(plan, qp, kp, band, local_stride, global_stride, alpha=0.9,
     loc = arm_recall(plan, qp, kp, True, local_stride, TEMPORAL, band, tau, scale)
     glo = arm_recall(plan, qp, kp, False, global_stride, SPATIAL, band, tau, scale)
     return arm_classify(loc, glo, alpha)
+
+
+def quantize_fp8(plan, xp, order=ROWS, out=None, scale=None):
+    """e4m3 codes (uint8, same shape as xp) and power-of-two scales of a
+    permuted bf16 tensor: per tile for RF_ROWS ([B, H, n_tiles]), per
+    feature for RF_TILES_T ([B, H, d])."""
+    B, H = xp.shape[:2]
+    d = xp.shape[3]
+    if out is None:
+        out = torch.empty(xp.shape, dtype=torch.uint8, device=xp.device)
+    if scale is None:
+        n = plan.sizes["n_tiles"] if order == ROWS else d
+        scale = torch.empty((B, H, n), dtype=torch.float32, device=xp.device)
+    _check(lib().rf_quantize_fp8(plan.handle, _ptr(xp), order, _ptr(out), _ptr(scale),
+                                 B, H, d, _dtype_code(xp), _stream()), "rf_quantize_fp8")
+    return out, scale
+
+
+def sparse_attn_fp8(plan, q8, qs, k8, ks, v8, vs, kept, sparsity_pct, scale=None,
+                    out=None):
+    """Block-sparse attention on e4m3 operands; bf16 output [B, H, Lt, d]."""
+    B, H, _, d = q8.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
+    _check(lib().rf_sparse_attn_fp8(plan.handle, _ptr(q8), _ptr(qs), _ptr(k8), _ptr(ks),
+                                    _ptr(v8), _ptr(vs), _ptr(kept), int(sparsity_pct),
+                                    _ptr(out), B, H, d, float(scale), _stream()),
+           "rf_sparse_attn_fp8")
+    return out
+
+
+def sparse_attn_fp8_rows(plan, q8, qs, k8, ks, v8, vs, rows, scale=None, out=None):
+    B, H, _, d = q8.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
+    _check(lib().rf_sparse_attn_fp8_rows(plan.handle, _ptr(q8), _ptr(qs), _ptr(k8),
+                                         _ptr(ks), _ptr(v8), _ptr(vs), _ptr(rows),
+                                         rows.shape[-1], _ptr(out), B, H, d, float(scale),
+                                         _stream()), "rf_sparse_attn_fp8_rows")
+    return out
+
+
+def sparse_attention_fp8(q, k, v, plan, sparsity_pct, scale=None):
+    """The whole path with the FP8 attention: permute and pool (bf16),
+    predict, quantize Q, K, V, attend, unpermute.  Returns (o, kept)."""
+    qp, qbar = permute_means(plan, q)
+    kp, kbar = permute_means(plan, k)
+    vt = permute(plan, v, order=TILES_T)
+    kept = predict_mask(plan, qbar, kbar, sparsity_pct)
+    q8, qs = quantize_fp8(plan, qp)
+    k8, ks = quantize_fp8(plan, kp)
+    v8, vs = quantize_fp8(plan, vt, order=TILES_T)
+    op = sparse_attn_fp8(plan, q8, qs, k8, ks, v8, vs, kept, sparsity_pct, scale=scale)
+    return unpermute(plan, op), kept
 
 
 def padded_rows(rows):

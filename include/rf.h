@@ -326,6 +326,52 @@ rf_status rf_arm_classify(const float* local_recall, int32_t n_local,
                           int32_t BH, float alpha, int32_t* head_pattern,
                           float* mean_or_null, hipStream_t stream);
 
+/* ---- FP8 variant -------------------------------------------------------- */
+
+/* e4m3 operands for the FP8 attention [RF2 TL;DR: integration with
+ * quantization named as future work].  OCP e4m3 codes (1 sign, 4 exponent
+ * bits with bias 7, 3 mantissa bits; largest finite 448), rounded to
+ * nearest, ties to even, from x * 2^-e with one power-of-two scale 2^e per
+ * group, e the smallest integer with amax <= 448 * 2^e (e = 0 for an
+ * all-zero group).  Groups:
+ *   order RF_ROWS:    xp [B][H][Lt][d] -> x8 [B][H][Lt][d] uint8, one scale
+ *                     per (b, h, tile): scale fp32 [B][H][n_tiles] = 2^e;
+ *   order RF_TILES_T: xp [B][H][n_tiles][d][bs] -> x8 in the same order, one
+ *                     scale per (b, h, feature) over all slots: scale fp32
+ *                     [B][H][d] (used as scratch while the call runs).
+ * xp is bf16 (RF_BF16 only) with finite values; x8 16-byte aligned. */
+rf_status rf_quantize_fp8(const rf_plan* plan, const void* xp, rf_order order,
+                          void* x8, float* scale, int32_t B, int32_t H,
+                          int32_t d, rf_dtype dtype, hipStream_t stream);
+
+/* Block-sparse attention on e4m3 operands: q8, k8 [B][H][Lt][d] (RF_ROWS)
+ * with per-tile scales q_scale, k_scale [B][H][n_tiles]; v8
+ * [B][H][n_tiles][d][bs] (RF_TILES_T) with per-feature scales v_scale
+ * [B][H][d] (16-byte aligned), all from rf_quantize_fp8.  For each valid
+ * query slot: o = sum_j w_j (v8_j * v_scale) / sum_j w_j over the valid
+ * slots of the kept tiles, w_j = the e4m3 rounding of the softmax weight of
+ * logit scale * (q8 . k8_j) * q_scale * k_scale, accumulated in fp32; op
+ * bf16 [B][H][Lt][d], pad query rows 0.  kept_idx and sparsity_pct as for
+ * rf_sparse_attn.  d = 128 and bs = 128 only (RF_ERR_UNSUPPORTED
+ * otherwise). */
+rf_status rf_sparse_attn_fp8(const rf_plan* plan, const void* q8,
+                             const float* q_scale, const void* k8,
+                             const float* k_scale, const void* v8,
+                             const float* v_scale, const int32_t* kept_idx,
+                             int32_t sparsity_pct, void* op, int32_t B,
+                             int32_t H, int32_t d, float scale,
+                             hipStream_t stream);
+
+/* rf_sparse_attn_fp8 on padded kept rows (the layout of
+ * rf_sparse_attn_rows). */
+rf_status rf_sparse_attn_fp8_rows(const rf_plan* plan, const void* q8,
+                                  const float* q_scale, const void* k8,
+                                  const float* k_scale, const void* v8,
+                                  const float* v_scale,
+                                  const int32_t* kept_rows, int32_t row_width,
+                                  void* op, int32_t B, int32_t H, int32_t d,
+                                  float scale, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -141,6 +141,12 @@ def test_gpu_entry_points_reject_bad_arguments_without_a_device():
     assert L.rf_pattern_mask(None, buf, 1, 1, 2, 2, buf, 8, None) == rf.ERR_INVALID_ARG
     assert L.rf_arm_recall(None, buf, buf, 1, 4, rf.TEMPORAL, 2, 2, 1, 1, 64, 0.125,
                            rf.BF16, buf, None) == rf.ERR_INVALID_ARG
+    assert L.rf_quantize_fp8(None, buf, rf.ROWS, buf, buf, 1, 1, 128, rf.BF16,
+                             None) == rf.ERR_INVALID_ARG
+    assert L.rf_sparse_attn_fp8(None, buf, buf, buf, buf, buf, buf, buf, 50, buf, 1, 1,
+                                128, 0.125, None) == rf.ERR_INVALID_ARG
+    assert L.rf_sparse_attn_fp8_rows(None, buf, buf, buf, buf, buf, buf, buf, 4, buf, 1,
+                                     1, 128, 0.125, None) == rf.ERR_INVALID_ARG
     assert b"null plan" in L.rf_last_error()
     # The classifier needs no plan: its sizes are checked first.
     assert L.rf_arm_classify(buf, 0, buf, 4, 1, 0.9, buf, None, None) == rf.ERR_INVALID_ARG
