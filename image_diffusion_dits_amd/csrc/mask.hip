@@ -9,9 +9,13 @@
 // is ranking by the softmax score.
 //
 // One workgroup serves R query rows of one head:
-//   1. the R rows of qbar go to LDS; each thread owns key blocks j and
-//      accumulates R dot products in fp32 (kbar_j streamed once per R rows,
-//      qbar read by LDS broadcast); the R x nb dots stay in LDS;
+//   1. the R x nb dot products, kept in LDS.  Up to 1024 blocks per row:
+//      R = 16 (three workgroups per CU for the selection below to spread
+//      over) and the dots come from fp32 MFMA (v_mfma_f32_16x16x4_f32), each
+//      wave taking every fourth group of 16 keys with the query rows held in
+//      registers.  Beyond that: R = 4 and every thread
+//      owns key blocks and accumulates R dots with fp32 FMA (query rows read
+//      by LDS broadcast);
 //   2. each wave selects for its rows: an exact k-th-largest search over the
 //      order-preserving integer image of the fp32 dots (32 bisection steps of
 //      wave-wide ballots), then an ascending ballot/prefix-count compaction
@@ -42,22 +46,33 @@ __device__ inline int popc64(uint64_t m) { return __popcll(m); }
 //        kept set is {key >= t} and the search stops.
 //   keep key > tau, and of the keys == tau the lowest-indexed
 //   k_sel - #{key > tau}; the ascending compaction is a ballot prefix count.
+// The sink bits of lane l's blocks l + 64 m (bit m), the same for every row:
+// loaded once per wave, all loads in flight together.
 template <int MMAX>
-__device__ void select_row(const float* __restrict__ row,
-                           const uint8_t* __restrict__ is_sink, int nb,
-                           int k_sel, int k_eff, int n_tt,
-                           int32_t* __restrict__ out, int lane) {
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  uint32_t key[MMAX];
+__device__ __attribute__((always_inline)) uint32_t sink_bits(const uint8_t* __restrict__ is_sink,
+                                                             int nb, int lane) {
   uint32_t sinkm = 0;
 #pragma unroll
   for (int m = 0; m < MMAX; ++m) {
     const int j = lane + 64 * m;
-    key[m] = 0;
-    if (j < nb) {
-      if (is_sink[j]) sinkm |= 1u << m;
-      else key[m] = order_key(row[j]);
-    }
+    const uint32_t sk = is_sink[min(j, nb - 1)];
+    sinkm |= uint32_t(j < nb && sk != 0) << m;
+  }
+  return sinkm;
+}
+
+template <int MMAX>
+__device__ __attribute__((always_inline)) void select_row(const float* __restrict__ row,
+                                                          uint32_t sinkm, int nb, int k_sel,
+                                                          int k_eff, int n_tt,
+                                                          int32_t* __restrict__ out, int lane) {
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint32_t key[MMAX];
+#pragma unroll
+  for (int m = 0; m < MMAX; ++m) {
+    const int j = lane + 64 * m;
+    const uint32_t k = order_key(row[min(j, nb - 1)]);
+    key[m] = (j < nb && !((sinkm >> m) & 1u)) ? k : 0u;
   }
   uint32_t tau = 0;
   if (k_sel > 0) {
@@ -142,10 +157,84 @@ __global__ __launch_bounds__(kThreads) void predict_mask_kernel(
 
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   const int k_sel = k_eff - n_sink;
+  const uint32_t sinkm = sink_bits<MMAX>(is_sink, nb, lane);
   for (int r = wave; r < R; r += kWaves) {
     const int i = i0 + r;
     if (i >= nb) break;
-    select_row<MMAX>(sc + r * nb, is_sink, nb, k_sel, k_eff, n_tt,
+    select_row<MMAX>(sc + r * nb, sinkm, nb, k_sel, k_eff, n_tt,
+                     kept + bh * nnz + int64_t(i) * row_len, lane);
+  }
+}
+
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+// Dots on MFMA for R = 16 query rows and 16 key blocks at a time
+// (v_mfma_f32_16x16x4_f32).  Lane (li, q) = (lane % 16, lane / 16) supplies
+// A[i = li][k] = qbar[i0 + li][k] and B[k][j = li] = kbar[j0 + li][k] for
+// the k = 16c + 4q + e (c < D/16, e < 4) it loads as float4; the product
+// sums over all k whatever their order, and accumulator register r holds
+// row 4q + r, column li.
+template <int D, int MMAX>
+__global__ __launch_bounds__(kThreads) void predict_mask_mfma_kernel(
+    const float* __restrict__ qbar, const float* __restrict__ kbar,
+    const uint8_t* __restrict__ is_sink, int32_t* __restrict__ kept,
+    float* __restrict__ logits, int32_t nb, int32_t n_sink, int32_t k_eff,
+    int32_t n_tt, int32_t row_len, int64_t nnz, float scale) {
+  constexpr int R = 16;
+  extern __shared__ float sc[];          // [R][nb]
+  const int64_t bh = blockIdx.y;
+  const int i0 = blockIdx.x * R;
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int li = lane % 16, q = lane / 16;
+  const float* qh = qbar + bh * nb * D;
+  const float* kh = kbar + bh * nb * D;
+  float4 qf[D / 16];
+  {
+    const float4* qr = reinterpret_cast<const float4*>(qh + int64_t(min(i0 + li, nb - 1)) * D);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) qf[c] = qr[4 * c + q];
+  }
+  const int nkb = (nb + 15) / 16;
+  // The next block's key rows are loaded while this block's MFMAs run.
+  auto load_keys = [&](int kb, float4 (&kf)[D / 16]) {
+    const float4* kr =
+        reinterpret_cast<const float4*>(kh + int64_t(min(kb * 16 + li, nb - 1)) * D);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) kf[c] = kr[4 * c + q];
+  };
+  float4 kn[D / 16];
+  if (wave < nkb) load_keys(wave, kn);
+  for (int kb = wave; kb < nkb; kb += kWaves) {
+    const int j = kb * 16 + li;
+    float4 kf[D / 16];
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) kf[c] = kn[c];
+    if (kb + kWaves < nkb) load_keys(kb + kWaves, kn);
+    f32x4v acc = {};
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[c].x, kf[c].x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[c].y, kf[c].y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[c].z, kf[c].z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[c].w, kf[c].w, acc, 0, 0, 0);
+    }
+    if (j < nb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * q + r;
+        sc[i * nb + j] = acc[r];
+        if (logits != nullptr && i0 + i < nb)
+          logits[(bh * nb + i0 + i) * nb + j] = acc[r] * scale;
+      }
+    }
+  }
+  __syncthreads();
+  const int k_sel = k_eff - n_sink;
+  const uint32_t sinkm = sink_bits<MMAX>(is_sink, nb, lane);
+  for (int r = wave; r < R; r += kWaves) {
+    const int i = i0 + r;
+    if (i >= nb) break;
+    select_row<MMAX>(sc + r * nb, sinkm, nb, k_sel, k_eff, n_tt,
                      kept + bh * nnz + int64_t(i) * row_len, lane);
   }
 }
@@ -158,6 +247,33 @@ __global__ void text_rows_kernel(int32_t* __restrict__ kept, int32_t nb,
   int32_t* out = kept + bh * nnz + int64_t(nb) * row_len_video +
                  int64_t(blockIdx.x) * n_tiles;
   for (int t = threadIdx.x; t < n_tiles; t += blockDim.x) out[t] = t;
+}
+
+template <int D, int MMAX>
+void launch_mfma(const rf_plan* p, const float* qbar, const float* kbar,
+                 int32_t* kept, float* logits, int BH, const rf_keep& kc,
+                 hipStream_t st) {
+  const int nb = p->sz.nb;
+  const size_t lds = sizeof(float) * 16 * size_t(nb);
+  (void)hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&predict_mask_mfma_kernel<D, MMAX>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  dim3 grid((nb + 15) / 16, BH);
+  hipLaunchKernelGGL((predict_mask_mfma_kernel<D, MMAX>), grid, dim3(kThreads), lds, st,
+                     qbar, kbar, p->is_sink, kept, logits, nb, p->sz.n_sink,
+                     kc.k_eff, p->sz.n_text_tiles, kc.row_len_video,
+                     kc.nnz_per_head, 1.0f / sqrtf(float(D)));
+}
+
+template <int D>
+void launch_mfma_any(const rf_plan* p, const float* qbar, const float* kbar,
+                     int32_t* kept, float* logits, int BH, const rf_keep& kc,
+                     hipStream_t st) {
+  const int chunks = (p->sz.nb + 63) / 64;
+  if (chunks <= 4) launch_mfma<D, 4>(p, qbar, kbar, kept, logits, BH, kc, st);
+  else if (chunks <= 8) launch_mfma<D, 8>(p, qbar, kbar, kept, logits, BH, kc, st);
+  else if (chunks <= 12) launch_mfma<D, 12>(p, qbar, kbar, kept, logits, BH, kc, st);
+  else launch_mfma<D, 16>(p, qbar, kbar, kept, logits, BH, kc, st);
 }
 
 template <int D, int R, int MMAX>
@@ -198,9 +314,9 @@ extern "C" rf_status rf_predict_mask(const rf_plan* plan, const float* qbar,
   const int BH = B * H;
   // Rows per workgroup R: their dots must fit in LDS next to the R query
   // rows.  MMAX: register chunks per lane for the selection (nb <= 64 MMAX).
-  if (nb <= 1024 && sizeof(float) * 16 * (size_t(nb) + d) <= budget) {
-    if (d == 128) launch<128, 16, 16>(plan, qbar, kbar, kept_idx, logits_or_null, BH, kc, stream);
-    else launch<64, 16, 16>(plan, qbar, kbar, kept_idx, logits_or_null, BH, kc, stream);
+  if (nb <= 1024) {
+    if (d == 128) launch_mfma_any<128>(plan, qbar, kbar, kept_idx, logits_or_null, BH, kc, stream);
+    else launch_mfma_any<64>(plan, qbar, kbar, kept_idx, logits_or_null, BH, kc, stream);
   } else if (nb <= 4096 && sizeof(float) * 4 * (size_t(nb) + d) <= budget) {
     if (d == 128) launch<128, 4, 64>(plan, qbar, kbar, kept_idx, logits_or_null, BH, kc, stream);
     else launch<64, 4, 64>(plan, qbar, kbar, kept_idx, logits_or_null, BH, kc, stream);

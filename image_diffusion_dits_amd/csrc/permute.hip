@@ -82,13 +82,25 @@ __global__ __launch_bounds__(kThreads) void permute_tiles_t_kernel(
   const int64_t bh = blockIdx.y;
   const int32_t tile = blockIdx.x;
   const uint8_t* src = x + bh * L * (D * E);
-  for (int c = threadIdx.x; c < BS * CPR; c += kThreads) {
+  // All of the thread's row chunks are loaded before any is stored, so the
+  // gathers of a workgroup are in flight together.
+  constexpr int NC = BS * CPR / kThreads;
+  static_assert(BS * CPR % kThreads == 0, "chunk split");
+  uint4 v[NC];
+#pragma unroll
+  for (int u = 0; u < NC; ++u) {
+    const int c = threadIdx.x + u * kThreads;
     const int s = c / CPR, k = c % CPR;
     const int32_t tok = slot_src[int64_t(tile) * BS + s];
-    uint4 v = make_uint4(0, 0, 0, 0);
+    v[u] = make_uint4(0, 0, 0, 0);
     if (tok >= 0)
-      v = *reinterpret_cast<const uint4*>(src + int64_t(tok) * (D * E) + k * 16);
-    *reinterpret_cast<uint4*>(lds + s * ROW + k * 16) = v;
+      v[u] = *reinterpret_cast<const uint4*>(src + int64_t(tok) * (D * E) + k * 16);
+  }
+#pragma unroll
+  for (int u = 0; u < NC; ++u) {
+    const int c = threadIdx.x + u * kThreads;
+    const int s = c / CPR, k = c % CPR;
+    *reinterpret_cast<uint4*>(lds + s * ROW + k * 16) = v[u];
   }
   __syncthreads();
   // Sub-block (fc, sc): features fc*VE.., slots sc*VE..
