@@ -362,9 +362,10 @@ def main():
         ks = torch.empty_like(qs)
         vs = torch.empty(B, H, d, dtype=torch.float32, device=dev)
 
-    stages = ["permute_means_qk", "permute_v", "predict_mask"]
-    stages += ["quantize_fp8"] if a.fp8 else []
-    stages += ["sparse_attn", "unpermute"]
+    if a.fp8:
+        stages = ["permute_fp8_qk", "permute_fp8_v", "predict_mask", "sparse_attn", "unpermute"]
+    else:
+        stages = ["permute_means_qk", "permute_v", "predict_mask", "sparse_attn", "unpermute"]
     n_ev = len(stages) + 1
 
     def step(ev=None):
@@ -375,18 +376,20 @@ def main():
             if ev is not None:
                 ev[i].record()
         mark()
-        rf.permute_means(plan, q, out=qp, xbar=qbar)
-        rf.permute_means(plan, k, out=kp, xbar=kbar)
-        mark()
-        rf.permute(plan, v, order=rf.TILES_T, out=vt)
+        if a.fp8:
+            rf.permute_fp8(plan, q, means=True, out=q8, scale=qs, xbar=qbar)
+            rf.permute_fp8(plan, k, means=True, out=k8, scale=ks, xbar=kbar)
+            mark()
+            rf.permute_fp8(plan, v, order=rf.TILES_T, out=v8, scale=vs)
+        else:
+            rf.permute_means(plan, q, out=qp, xbar=qbar)
+            rf.permute_means(plan, k, out=kp, xbar=kbar)
+            mark()
+            rf.permute(plan, v, order=rf.TILES_T, out=vt)
         mark()
         rf.predict_mask(plan, qbar, kbar, s, kept=kept)
         mark()
         if a.fp8:
-            rf.quantize_fp8(plan, qp, out=q8, scale=qs)
-            rf.quantize_fp8(plan, kp, out=k8, scale=ks)
-            rf.quantize_fp8(plan, vt, order=rf.TILES_T, out=v8, scale=vs)
-            mark()
             rf.sparse_attn_fp8(plan, q8, qs, k8, ks, v8, vs, kept, s, out=op)
         else:
             rf.sparse_attn(plan, qp, kp, vt, kept, s, out=op)
@@ -435,6 +438,8 @@ def main():
     esize = 2 if cfg.dtype == "bf16" else 4
     perm_bytes = B * H * (z["L"] + z["Lt"]) * d * esize   # one tensor
     unperm_bytes = B * H * 2 * z["L"] * d * esize
+    perm8_bytes = B * H * (z["L"] * esize + z["Lt"]) * d      # bf16 in, e4m3 out
+    perm8v_bytes = B * H * (2 * z["L"] * esize + z["Lt"]) * d  # maxima pass, then one pass
 
     rec = {
         "metric": METRIC,
@@ -465,11 +470,15 @@ def main():
         "stages_ms": {n: round(x, 4) for n, x in stage_ms.items()},
         "event_ms_per_step": round(ev_step_ms, 4),
         "mask_plus_perm_over_attn": round(aux_ms / stage_ms["sparse_attn"], 4),
-        "hbm_gbs": {
+        "hbm_gbs": ({
+            "permute_fp8_qk": round(2 * perm8_bytes / (stage_ms["permute_fp8_qk"] / 1e3) / 1e9, 1),
+            "permute_fp8_v": round(perm8v_bytes / (stage_ms["permute_fp8_v"] / 1e3) / 1e9, 1),
+            "unpermute": round(unperm_bytes / (stage_ms["unpermute"] / 1e3) / 1e9, 1),
+        } if a.fp8 else {
             "permute_means_qk": round(2 * perm_bytes / (stage_ms["permute_means_qk"] / 1e3) / 1e9, 1),
             "permute_v": round(perm_bytes / (stage_ms["permute_v"] / 1e3) / 1e9, 1),
             "unpermute": round(unperm_bytes / (stage_ms["unpermute"] / 1e3) / 1e9, 1),
-        },
+        }),
         "roofline": {
             "kernel": ("attn_fp8_pp_kernel" if a.fp8 else
                        "attn_bf16_pp_kernel" if cfg.dtype == "bf16" else "attn_f32_kernel"),
@@ -484,6 +493,9 @@ def main():
     if a.fp8:
         # Cost of the e4m3 operands: the same step's output against the bf16
         # attention on the same permuted tensors.
+        rf.permute(plan, q, out=qp)
+        rf.permute(plan, k, out=kp)
+        rf.permute(plan, v, order=rf.TILES_T, out=vt)
         ref = rf.sparse_attn(plan, qp, kp, vt, kept, s)
         torch.cuda.synchronize()
         diff = (op.float() - ref.float()).abs()

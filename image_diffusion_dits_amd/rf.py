@@ -88,6 +88,8 @@ _SIGNATURES = {
                         _vp],
     "rf_quantize_fp8": [_vp, _vp, ctypes.c_int, _vp, _vp, _c_i32, _c_i32, _c_i32,
                         ctypes.c_int, _vp],
+    "rf_permute_fp8": [_vp, _vp, ctypes.c_int, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32,
+                       ctypes.c_int, _vp],
     "rf_sparse_attn_fp8": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _vp,
                            _c_i32, _c_i32, _c_i32, _c_f32, _vp],
     "rf_sparse_attn_fp8_rows": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i32,
@@ -468,6 +470,28 @@ def quantize_fp8(plan, xp, order=ROWS, out=None, scale=None):
     return out, scale
 
 
+def permute_fp8(plan, x, order=ROWS, means=False, out=None, scale=None, xbar=None):
+    """Permuted e4m3 codes and scales of a raster bf16 tensor in one pass
+    (and, for RF_ROWS with means=True, the block means).  Returns
+    (codes, scale) or (codes, scale, xbar)."""
+    B, H, d = _bhd(x)
+    z = plan.sizes
+    if x.shape[2] != z["L"]:
+        raise ValueError(f"x has {x.shape[2]} tokens, layout needs {z['L']}")
+    if out is None:
+        shape = (B, H, z["Lt"], d) if order == ROWS else (B, H, z["n_tiles"], d, z["bs"])
+        out = torch.empty(shape, dtype=torch.uint8, device=x.device)
+    if scale is None:
+        n = z["n_tiles"] if order == ROWS else d
+        scale = torch.empty((B, H, n), dtype=torch.float32, device=x.device)
+    if means and xbar is None:
+        xbar = torch.empty((B, H, z["nb"], d), dtype=torch.float32, device=x.device)
+    _check(lib().rf_permute_fp8(plan.handle, _ptr(x), order, _ptr(out), _ptr(scale),
+                                _ptr(xbar) if means else None, B, H, d, _dtype_code(x),
+                                _stream()), "rf_permute_fp8")
+    return (out, scale, xbar) if means else (out, scale)
+
+
 def sparse_attn_fp8(plan, q8, qs, k8, ks, v8, vs, kept, sparsity_pct, scale=None,
                     out=None):
     """Block-sparse attention on e4m3 operands; bf16 output [B, H, Lt, d]."""
@@ -497,15 +521,13 @@ def sparse_attn_fp8_rows(plan, q8, qs, k8, ks, v8, vs, rows, scale=None, out=Non
 
 
 def sparse_attention_fp8(q, k, v, plan, sparsity_pct, scale=None):
-    """The whole path with the FP8 attention: permute and pool (bf16),
-    predict, quantize Q, K, V, attend, unpermute.  Returns (o, kept)."""
-    qp, qbar = permute_means(plan, q)
-    kp, kbar = permute_means(plan, k)
-    vt = permute(plan, v, order=TILES_T)
+    """The whole path with the FP8 attention: permute into e4m3 codes and
+    pool (one pass per tensor), predict, attend, unpermute.  Returns
+    (o, kept)."""
+    q8, qs, qbar = permute_fp8(plan, q, means=True)
+    k8, ks, kbar = permute_fp8(plan, k, means=True)
+    v8, vs = permute_fp8(plan, v, order=TILES_T)
     kept = predict_mask(plan, qbar, kbar, sparsity_pct)
-    q8, qs = quantize_fp8(plan, qp)
-    k8, ks = quantize_fp8(plan, kp)
-    v8, vs = quantize_fp8(plan, vt, order=TILES_T)
     op = sparse_attn_fp8(plan, q8, qs, k8, ks, v8, vs, kept, sparsity_pct, scale=scale)
     return unpermute(plan, op), kept
 

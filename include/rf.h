@@ -344,6 +344,19 @@ rf_status rf_quantize_fp8(const rf_plan* plan, const void* xp, rf_order order,
                           void* x8, float* scale, int32_t B, int32_t H,
                           int32_t d, rf_dtype dtype, hipStream_t stream);
 
+/* rf_permute (or rf_permute_means) fused with rf_quantize_fp8: the raster
+ * bf16 tensor x [B][H][L][d] goes straight to permuted e4m3 codes x8 and
+ * scales, bit for bit those of rf_permute followed by rf_quantize_fp8 with
+ * the same order; for RF_ROWS, xbar_or_null (fp32 [B][H][nb][d], or null)
+ * receives the block means of the bf16 values, bit for bit those of
+ * rf_permute_means.  RF_TILES_T takes no xbar.  One pass over x for
+ * RF_ROWS; for RF_TILES_T a read of x for the feature maxima, then one
+ * pass. */
+rf_status rf_permute_fp8(const rf_plan* plan, const void* x, rf_order order,
+                         void* x8, float* scale, float* xbar_or_null,
+                         int32_t B, int32_t H, int32_t d, rf_dtype dtype,
+                         hipStream_t stream);
+
 /* Block-sparse attention on e4m3 operands: q8, k8 [B][H][Lt][d] (RF_ROWS)
  * with per-tile scales q_scale, k_scale [B][H][n_tiles]; v8
  * [B][H][n_tiles][d][bs] (RF_TILES_T) with per-feature scales v_scale

@@ -302,3 +302,27 @@ def test_fp8_deterministic_and_errors():
         rf.sparse_attn_fp8(plan64, x8, xs, x8, xs, v8, vsc, kept, 0)
     plan.close()
     plan64.close()
+
+
+@pytest.mark.parametrize("case", EDGE[:3] + [("video720-2heads", configs.VIDEO720.layout, 1, 2, 80)],
+                         ids=[c[0] for c in EDGE[:3]] + ["video720-2heads"])
+def test_fused_permute_fp8_matches_two_steps(case):
+    """rf_permute_fp8 gives the bytes of rf_permute + rf_quantize_fp8 and the
+    means of rf_permute_means."""
+    name, lay, B, H, _ = case
+    say(f"[fp8 fused permute] {name}")
+    z = rf.layout_sizes(lay)
+    plan = rf.Plan(lay)
+    x = _iid((B, H, z["L"], 128), 77)
+    xp, xbar = rf.permute_means(plan, x)
+    c1, s1 = rf.quantize_fp8(plan, xp)
+    c2, s2, xbar2 = rf.permute_fp8(plan, x, means=True)
+    vt = rf.permute(plan, x, order=rf.TILES_T)
+    c3, s3 = rf.quantize_fp8(plan, vt, order=rf.TILES_T)
+    c4, s4 = rf.permute_fp8(plan, x, order=rf.TILES_T)
+    c5, s5 = rf.permute_fp8(plan, x)                     # no means
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2) and torch.equal(s1, s2) and torch.equal(xbar, xbar2)
+    assert torch.equal(c3, c4) and torch.equal(s3, s4)
+    assert torch.equal(c1, c5) and torch.equal(s1, s5)
+    plan.close()
