@@ -32,7 +32,13 @@ PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3
 PEAK_FP8_TFLOPS = 5000.0        # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0
-ATTN_SRC = os.path.join(ROOT, "image_diffusion_dits_amd", "csrc", "attn.hip")
+CSRC = os.path.join(ROOT, "image_diffusion_dits_amd", "csrc")
+# Sources each attention kernel is compiled from (its file and the headers it
+# includes): stored counter readings apply only while these are unchanged.
+KERNEL_SOURCES = {
+    "attn_bf16_pp_kernel": ["attn.hip", "tile_common.h", "rf_internal.h"],
+    "attn_fp8_pp_kernel": ["attn_fp8.hip", "tile_common.h", "rf_internal.h"],
+}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
 
 
@@ -244,20 +250,23 @@ def recall_study(n_sample):
     return 0
 
 
-def source_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def source_hash(kernel):
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
-def stored_traffic(workload, per_launch_flop):
+def stored_traffic(kernel, workload):
     """HBM bytes per attention launch from committed rocprofv3 counter runs,
     or None when absent or taken on a different kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)
+            rec = json.load(f).get(kernel, {})
     except (OSError, ValueError):
         return None
-    if rec.get("attn_src_sha256") != source_hash(ATTN_SRC):
+    if kernel not in KERNEL_SOURCES or rec.get("src_sha256") != source_hash(kernel):
         return None
     if rec.get("workload") != workload:
         return None
@@ -433,7 +442,9 @@ def main():
         peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
     attn_tflops = exec_flop / attn_s / 1e12
     workload = cfg.name + ("" if cfg.permute else "-raster")
-    traffic = None if a.fp8 else stored_traffic(workload, exec_flop)
+    kernel = ("attn_fp8_pp_kernel" if a.fp8 else
+              "attn_bf16_pp_kernel" if cfg.dtype == "bf16" else "attn_f32_kernel")
+    traffic = stored_traffic(kernel, workload)
     aux_ms = sum(stage_ms[n] for n in stages if n != "sparse_attn")
     esize = 2 if cfg.dtype == "bf16" else 4
     perm_bytes = B * H * (z["L"] + z["Lt"]) * d * esize   # one tensor
@@ -480,8 +491,7 @@ def main():
             "unpermute": round(unperm_bytes / (stage_ms["unpermute"] / 1e3) / 1e9, 1),
         }),
         "roofline": {
-            "kernel": ("attn_fp8_pp_kernel" if a.fp8 else
-                       "attn_bf16_pp_kernel" if cfg.dtype == "bf16" else "attn_f32_kernel"),
+            "kernel": kernel,
             "bound": "mfma",
             "achieved": round(attn_tflops, 2),
             "peak": peak,

@@ -262,10 +262,18 @@ __global__ __launch_bounds__(kThreads) void raster_amax_kernel(
   const int64_t r1 = min(L, r0 + rows_per_chunk);
   typedef uint16_t u16x8 __attribute__((__vector_size__(16)));
   float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int64_t r = r0 + rg; r < r1; r += RG) {
-    const u16x8 w = *reinterpret_cast<const u16x8*>(x + (bh * L + r) * D + k * 8);
+  // Four rows per thread in flight at a time.
+  for (int64_t r = r0 + rg; r < r1; r += 4 * RG) {
+    u16x8 w[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) m[e] = fmaxf(m[e], fabsf(bf16_to_f32(w[e])));
+    for (int u = 0; u < 4; ++u) {
+      const int64_t rr = min(r + u * RG, r1 - 1);
+      w[u] = *reinterpret_cast<const u16x8*>(x + (bh * L + rr) * D + k * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m[e] = fmaxf(m[e], fabsf(bf16_to_f32(w[u][e])));
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) part[rg][k * 8 + e] = m[e];
@@ -347,7 +355,7 @@ void launch_permute_fp8(const rf_plan* p, const void* x, rf_order order, void* x
   const int64_t n = int64_t(BH) * D;
   uint32_t* am = reinterpret_cast<uint32_t*>(scale);
   hipLaunchKernelGGL(zero_kernel, dim3((n + 255) / 256), dim3(256), 0, st, am, n);
-  const int32_t rows = 4096;
+  const int32_t rows = 512;
   hipLaunchKernelGGL((raster_amax_kernel<D>), dim3(BH, (p->sz.L + rows - 1) / rows),
                      dim3(kThreads), 0, st, xs, am, p->sz.L, rows);
   hipLaunchKernelGGL((permute_quant_tiles_t_kernel<D, BS>), dim3(nt, BH), dim3(kThreads), 0, st,
