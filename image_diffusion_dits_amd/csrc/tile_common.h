@@ -62,17 +62,22 @@ constexpr int kBufferWord3 = 0x00020000;
 // Copies one tile of `bytes` bytes at `base` into LDS at `dst` through a
 // buffer resource spanning exactly the tile: copy u of group wave w writes
 // LDS [dst + (u*WAVES + w) * 1024, +1024) from lane offset voff + u * the
-// bytes one copy covers.
+// bytes one copy covers.  The wave's offset passes through an empty asm so
+// that the compiler recomputes the LDS addresses at each call instead of
+// keeping every one of them in a scalar register across the loop (which
+// spilled them to VGPR lanes).
 template <int COPIES, int WAVES>
 __device__ __forceinline__ void dma_tile(const char* base, int bytes, void* dst,
                                          uint32_t voff, int w) {
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, bytes, kBufferWord3);
   constexpr int kStride = WAVES * 64 * 16;
+  int woff = w * 1024;
+  asm volatile("" : "+s"(woff));
 #pragma unroll
   for (int u = 0; u < COPIES; ++u)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rsrc, (lds_void*)(static_cast<char*>(dst) + (u * WAVES + w) * 1024), 16, voff,
+        rsrc, (lds_void*)(static_cast<char*>(dst) + woff + u * WAVES * 1024), 16, voff,
         u * kStride, 0, 0);
 }
 
@@ -84,10 +89,12 @@ __device__ __forceinline__ void dma_tile_perm(const char* base, int bytes, void*
                                               const uint32_t (&soff)[COPIES]) {
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, bytes, kBufferWord3);
+  int woff = w * 1024;
+  asm volatile("" : "+s"(woff));
 #pragma unroll
   for (int u = 0; u < COPIES; ++u)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rsrc, (lds_void*)(static_cast<char*>(dst) + (u * WAVES + w) * 1024), 16, voff,
+        rsrc, (lds_void*)(static_cast<char*>(dst) + woff + u * WAVES * 1024), 16, voff,
         soff[u], 0, 0);
 }
 
