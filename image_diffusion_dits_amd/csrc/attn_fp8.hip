@@ -57,8 +57,11 @@ __device__ inline i32x8 lds32(const uint8_t* row, int c0, int swz) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Four e4m3 codes in one word.  The first conversion writes the low half and
+// keeps the high half of its `old` operand, which the second overwrites, so
+// `old` is any register (here a's): no zeroing move is needed.
 __device__ inline int pack4(float a, float b, float c, float d) {
-  int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
 }
 
