@@ -19,9 +19,10 @@
 //     The 32 weights of blocks 2s and 2s + 1 in lane group g are then keys
 //     64 s + 32 g .. +32 in order, which is exactly the 32-byte V^T run the
 //     same lane group reads for k-step s;
-//   * the row sum of the e4m3 weights comes from two more MFMAs with an
-//     all-ones A operand, so the normalisation uses the weights the PV
-//     product used and the vector ALU does not convert them back;
+//   * the row sum of the e4m3 weights comes from two more MFMAs whose A
+//     operand is 1 for valid and 0 for pad keys, so the normalisation uses
+//     the weights the PV product used, the vector ALU does not convert them
+//     back, and pad keys of partial tiles need no mask on the usual path;
 //   * logits are dot(q8, k8) * scale * 2^(eq + ek) (the key tile's scale
 //     enters the exp2 multiplier), and the feature scales of V multiply the
 //     output once at the end.
@@ -153,6 +154,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
     __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
   };
 
+  // Row-sum operand of the previous tile: e4m3 1.0 for every valid key, 0 for
+  // pad keys (whose weights need not be zero, see the VALU phase).  Byte e of
+  // k-step st in lane group g is key 64 st + 32 g + e: bit e of validity word
+  // 2 st + g, which the VALU phase leaves in vw[st] (all ones for a full
+  // tile), spread four bits per dword by a multiply.
+  uint32_t vw[2] = {~0u, ~0u};
+  bool vw_full = true;
+  auto row_sum_operand = [&](int st) -> i32x8 {
+    if (vw_full) return ones;
+    i32x8 a;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t nib = (vw[st] >> (4 * e)) & 0xfu;
+      a[e] = int(((nib * 0x00204081u) & 0x01010101u) * 0x38u);
+    }
+    return a;
+  };
+
   auto mfma_phase = [&](int32_t i) {
     if (i >= 1) {
       // O^T[db] += V^T[db rows, keys 64s .. +64] P^T(i-1), k-steps s = 0, 1.
@@ -162,8 +181,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
         for (int db = 0; db < D / 32; ++db)
           o[db] = mma(lds32(vs + (db * 32 + li) * kRowBytes, 4 * st + 2 * g, rswz), pb[st], o[db]);
       pipeline_reads();
-      lsum = mma(ones, pb[0], lsum);
-      lsum = mma(ones, pb[1], lsum);
+      lsum = mma(row_sum_operand(0), pb[0], lsum);
+      lsum = mma(row_sum_operand(1), pb[1], lsum);
     }
     __builtin_amdgcn_sched_barrier(0);
     if (i < n_grp) {
@@ -184,28 +203,42 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
     if (i + 1 < n_grp) copy_k(tile_of(i + 1));
     copy_v(kt);
     const int32_t tcount = kt >= 0 ? tile_count[kt] : 0;
-    if (tcount != BS) {
+    const float c = c_q * (kt >= 0 ? ksc[kt] : 1.f);
+    vw_full = tcount == BS;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) vw[st] = kt >= 0 ? tile_bits[kt * 4 + 2 * st + g] : 0u;
+    // Row max over the tile's raw dot products (the scale is positive).
+    auto row_max = [&]() {
+      float m = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < BS / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) m = fmaxf(m, s[kb][r]);
+      const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(m),
+                                                       __float_as_uint(m), false, false);
+      return fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));   // with lane ^ 32
+    };
+    float mx = row_max();
+    // Pad keys have all-zero K rows, so their scores are exactly 0, and
+    // all-zero V^T columns, so their weights add nothing to O; the row sum
+    // counts valid keys only.  When every query's tile maximum is positive it
+    // comes from a valid key, and a pad weight 2^(0 - m) stays within 2^8, so
+    // the pads need no mask.  Otherwise (and for a masked tile, kt < 0, whose
+    // copies hold tile 0) they are set to -inf.
+    if (tcount != BS && (kt < 0 || __ballot(!(mx > 0.f)) != 0)) {
       // Register r of block kb in lane group g is key 64(kb/2) + 32g +
       // 16(kb%2) + r: validity word 2(kb/2) + g, bit 16(kb%2) + r.
 #pragma unroll
       for (int kb = 0; kb < BS / 32; ++kb) {
-        const uint32_t bits =
-            (kt >= 0 ? tile_bits[kt * 4 + 2 * (kb / 2) + g] : 0u) >> (16 * (kb % 2));
+        const uint32_t pad =
+            ~((kt >= 0 ? tile_bits[kt * 4 + 2 * (kb / 2) + g] : 0u) >> (16 * (kb % 2)));
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (!((bits >> r) & 1u)) s[kb][r] = -INFINITY;
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t m = uint32_t(int32_t(pad << (31 - r)) >> 31);
+          s[kb][r] = __uint_as_float((m & 0xff800000u) | (~m & __float_as_uint(s[kb][r])));
+        }
       }
-    }
-    const float c = c_q * (kt >= 0 ? ksc[kt] : 1.f);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < BS / 32; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    {
-      const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx),
-                                                       __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+      mx = row_max();
     }
     const float mt = mx * c;
     if (__ballot(mt > m_run + 8.f) != 0) {
