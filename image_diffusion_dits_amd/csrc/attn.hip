@@ -509,29 +509,41 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
     if (i + 1 < n_grp) copy_k(tile_of(i + 1));
     copy_v(kt);
     const int32_t tcount = kt >= 0 ? tile_count[kt] : 0;
-    if (tcount != BS) {
-      // Keys of lane group g sit at bit 8g + (16(a/2) + 4(a%2) + b); a
-      // masked tile (kt < 0) has no valid key.
-#pragma unroll
-      for (int kb = 0; kb < BS / 32; ++kb) {
-        const uint32_t bits = (kt >= 0 ? tile_bits[kt * 4 + kb] : 0u) >> (8 * g);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int a = r / 4, b = r % 4;
-          if (!((bits >> (16 * (a / 2) + 4 * (a % 2) + b)) & 1u)) s[kb][r] = -INFINITY;
-        }
-      }
-    }
     // Row max over the tile (raw dot products; the scale is positive).
-    float mx = -INFINITY;
+    auto row_max = [&]() {
+      float m = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < BS / 32; ++kb)
+      for (int kb = 0; kb < BS / 32; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    {
-      const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx),
-                                                       __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));   // max with lane ^ 32
+        for (int r = 0; r < 16; ++r) m = fmaxf(m, s[kb][r]);
+      const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(m),
+                                                       __float_as_uint(m), false, false);
+      return fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));   // max with lane ^ 32
+    };
+    float mx = row_max();
+    // Pad keys have all-zero K rows, so they score exactly 0, and all-zero
+    // V^T columns, so their weights add nothing to O.  When every query's
+    // tile maximum is positive it comes from a valid key and a pad weight
+    // 2^(0 - m) stays within 2^8: the pads are left unmasked and their
+    // weights are taken out of the row sum afterwards.  Otherwise (and for a
+    // masked tile, kt < 0, whose copies hold tile 0) they are set to -inf.
+    bool pads_in_sum = false;
+    if (tcount != BS) {
+      if (kt < 0 || __ballot(!(mx > 0.f)) != 0) {
+        // Keys of lane group g sit at bit 8g + (16(a/2) + 4(a%2) + b).
+#pragma unroll
+        for (int kb = 0; kb < BS / 32; ++kb) {
+          const uint32_t bits = (kt >= 0 ? tile_bits[kt * 4 + kb] : 0u) >> (8 * g);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int a = r / 4, b = r % 4;
+            if (!((bits >> (16 * (a / 2) + 4 * (a % 2) + b)) & 1u)) s[kb][r] = -INFINITY;
+          }
+        }
+        mx = row_max();
+      } else {
+        pads_in_sum = true;
+      }
     }
     // Lazy rescaling: the running max only moves (and O, l are rescaled)
     // when some query's tile max exceeds it by more than 8 in log2 units;
@@ -566,6 +578,16 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
         lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 4, 5), one, lsum, false);
         lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 6, 7), one, lsum, false);
       }
+    }
+    if (pads_in_sum) {
+      // Each pad key of this lane's half of the tile (bits 8g + {0..7,
+      // 16..23} of each validity word) got the bf16 weight of 2^(0 - m).
+      uint32_t npad = 0;
+#pragma unroll
+      for (int kb = 0; kb < BS / 32; ++kb)
+        npad += __popc(~tile_bits[kt * 4 + kb] & (g ? 0xFF00FF00u : 0x00FF00FFu));
+      const float w_pad = float(__bf16(__builtin_amdgcn_exp2f(neg_m)));
+      lsum -= float(npad) * w_pad;
     }
     l_run = lsum;
     // The wait stays after the softmax, which it would otherwise precede.
