@@ -284,6 +284,49 @@ def sparse_attention(qp, kp, vp, kept, lay: Layout, scale=None,
     return out
 
 
+def attention_lse(qp, kp, kept, lay: Layout, scale=None, query_tiles=None):
+    """Natural log of each query's softmax denominator over its kept tiles,
+    fp64: lse = log sum_j exp(q . k_j * scale) over the valid tokens of
+    kept[b][h][i] (reading R8's sum); pad query slots are -inf, query tiles
+    not computed NaN.  qp, kp: [B, H, Np + n_text, d].  Returns [B, H, Lp]."""
+    z = sizes(lay)
+    bs, Lp = z["bs"], z["Lp"]
+    d = qp.shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    valid = slot_valid(lay)
+    B, H = qp.shape[:2]
+    out = np.full((B, H, Lp), np.nan)
+    for b in range(B):
+        for h in range(H):
+            tiles = (range(z["n_tiles"]) if query_tiles is None
+                     else query_tiles.get((b, h), ()))
+            for i in tiles:
+                rows = np.arange(i * bs, min((i + 1) * bs, Lp))
+                out[b, h, rows] = -np.inf
+                qrows = rows[valid[rows]]
+                keys = np.concatenate([np.arange(j * bs, min((j + 1) * bs, Lp))
+                                       for j in kept[b][h][i]])
+                keys = keys[valid[keys]]
+                s = (qp[b, h, qrows].astype(np.float64) @
+                     kp[b, h, keys].astype(np.float64).T) * scale
+                mx = s.max(axis=1, keepdims=True)
+                out[b, h, qrows] = (mx + np.log(np.exp(s - mx).sum(axis=1, keepdims=True)))[:, 0]
+    return out
+
+
+def kept_dense(kept, lay: Layout) -> np.ndarray:
+    """The kept lists as a 0/1 matrix [B, H, n_tiles, n_tiles] (row i, column
+    j = 1 when query tile i keeps key tile j)."""
+    z = sizes(lay)
+    B, H = len(kept), len(kept[0])
+    m = np.zeros((B, H, z["n_tiles"], z["n_tiles"]), dtype=np.uint8)
+    for b in range(B):
+        for h in range(H):
+            for i, row in enumerate(kept[b][h]):
+                m[b, h, i, np.asarray(row, dtype=np.int64)] = 1
+    return m
+
+
 def attention_recall(qp, kp, kept, lay: Layout, query_tiles, scale=None):
     """Share of each query's dense softmax mass inside its kept tiles, fp64.
 

@@ -814,3 +814,54 @@ def test_fp8_attention_is_exact_on_representable_inputs():
     a = orc.sparse_attention(qp, kp, vp, kept, lay)
     b = orc.sparse_attention_fp8(qp, kp, vp, kept, lay)
     np.testing.assert_array_equal(a, b)
+
+
+# ---------------------------------------------------------- LSE and dense mask
+
+@pytest.mark.parametrize("n_text,permute", [(0, 1), (5, 1), (3, 0)])
+def test_lse_zero_sparsity_is_dense_logsumexp(n_text, permute):
+    """With every tile kept the log-sum-exp is scipy's over the dense logits
+    of the raster sequence (library routine), slot by slot."""
+    lay = orc.Layout(3, 5, 7, 2, 2, 4, n_text=n_text, permute=permute, sink=1)
+    z = orc.sizes(lay)
+    r = _rng(89)
+    q, k = (r.standard_normal((1, 1, z["L"], 8)) for _ in range(2))
+    qp, kp = orc.permute(q, lay), orc.permute(k, lay)
+    nt = z["n_tiles"]
+    kept = [[[np.arange(nt)] * nt]]
+    lse = orc.attention_lse(qp, kp, kept, lay)
+    want = scipy.special.logsumexp(q[0, 0] @ k[0, 0].T / math.sqrt(8), axis=1)
+    got = lse[0, 0, orc.slot_of_token(lay).tolist() + list(range(z["Np"], z["Lp"]))]
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+    assert np.all(np.isneginf(lse[0, 0, ~orc.slot_valid(lay)]))
+
+
+def test_lse_of_zero_keys_is_log_count():
+    """k = 0 gives logits 0: lse = log(number of valid kept keys)."""
+    lay = orc.Layout(2, 6, 6, 1, 4, 4, n_text=3)
+    z = orc.sizes(lay)
+    r = _rng(97)
+    q = orc.permute(r.standard_normal((1, 1, z["L"], 4)), lay)
+    nt = z["n_tiles"]
+    kept = [[[np.sort(r.choice(nt, size=r.integers(1, nt + 1), replace=False))
+              for _ in range(nt)]]]
+    lse = orc.attention_lse(q, np.zeros_like(q), kept, lay)
+    counts = np.concatenate([orc.block_counts(lay),
+                             [min(z["bs"], lay.n_text - j * z["bs"])
+                              for j in range(z["n_text_tiles"])]])
+    valid = orc.slot_valid(lay)
+    for i in range(nt):
+        sl = slice(i * z["bs"], min((i + 1) * z["bs"], z["Lp"]))
+        np.testing.assert_allclose(lse[0, 0, sl][valid[sl]],
+                                   math.log(counts[kept[0][0][i]].sum()), atol=1e-14)
+
+
+def test_kept_dense_matches_rows():
+    lay = orc.Layout(2, 4, 4, 1, 2, 2, n_text=6, sink=1)
+    r = _rng(101)
+    qbar = r.standard_normal((1, 1, 8, 4))
+    kbar = r.standard_normal((1, 1, 8, 4))
+    kept, _ = orc.predict_mask(qbar, kbar, lay, 50)
+    m = orc.kept_dense(kept, lay)
+    for i, row in enumerate(kept[0][0]):
+        assert np.flatnonzero(m[0, 0, i]).tolist() == row.tolist()
