@@ -100,7 +100,8 @@ template <int D, int BS>
 __global__ __launch_bounds__((BS / 32) * 64, 2) void attn_bf16_kernel(
     const __bf16* __restrict__ qp, const __bf16* __restrict__ kp,
     const __bf16* __restrict__ vt, const int32_t* __restrict__ kept,
-    __bf16* __restrict__ op, const uint32_t* __restrict__ tile_bits,
+    __bf16* __restrict__ op, float* __restrict__ lse,
+    const uint32_t* __restrict__ tile_bits,
     const int32_t* __restrict__ tile_count, int64_t Lt, int32_t BH,
     int32_t nb, int32_t n_tt, int32_t row_len_video, int64_t nnz,
     float scale_log2) {
@@ -328,6 +329,7 @@ __global__ __launch_bounds__((BS / 32) * 64, 2) void attn_bf16_kernel(
   const int qs = wave * 32 + li;
   const bool qvalid = (tile_bits[qtile * 4 + qs / 32] >> (qs % 32)) & 1u;
   const float inv = (qvalid && l_tot > 0.f) ? 1.f / l_tot : 0.f;
+  if (lse != nullptr && g == 0) lse[bh * Lt + qrow] = lse_of(m_run, l_tot, qvalid);
   __bf16* dst = op + (bh * Lt + qrow) * D + 4 * g;
   typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 #pragma unroll
@@ -372,7 +374,8 @@ template <int D>
 __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
     const __bf16* __restrict__ qp, const __bf16* __restrict__ kp,
     const __bf16* __restrict__ vt, const int32_t* __restrict__ kept,
-    __bf16* __restrict__ op, const uint32_t* __restrict__ tile_bits,
+    __bf16* __restrict__ op, float* __restrict__ lse,
+    const uint32_t* __restrict__ tile_bits,
     const int32_t* __restrict__ tile_count, int64_t Lt, int32_t BH,
     int32_t nb, int32_t n_tt, int32_t row_len_video, int64_t nnz,
     float scale_log2) {
@@ -643,6 +646,7 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
   const bool qvalid = (tile_bits[qtile * 4 + qs / 32] >> (qs % 32)) & 1u;
   const float inv = (qvalid && l_tot > 0.f) ? 1.f / l_tot : 0.f;
   const float ca = fa * inv, cb = fb * inv;
+  if (lse != nullptr && g == 0) lse[bh * Lt + qrow] = lse_of(m_t, l_tot, qvalid);
   // Lane (li, g) holds O^T[dd = db*32 + 8a + 4g + b][query li].
   __bf16* dst = op + (bh * Lt + qrow) * D + 4 * g;
   typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
@@ -664,7 +668,8 @@ template <int D, int BS>
 __global__ __launch_bounds__(BS) void attn_f32_kernel(
     const float* __restrict__ qp, const float* __restrict__ kp,
     const float* __restrict__ vt, const int32_t* __restrict__ kept,
-    float* __restrict__ op, const uint32_t* __restrict__ tile_bits,
+    float* __restrict__ op, float* __restrict__ lse,
+    const uint32_t* __restrict__ tile_bits,
     const int32_t* __restrict__ tile_count, int64_t Lt, int32_t BH,
     int32_t nb, int32_t n_tt, int32_t row_len_video, int64_t nnz,
     float scale) {
@@ -738,6 +743,8 @@ __global__ __launch_bounds__(BS) void attn_f32_kernel(
   }
   const bool qvalid = (tile_bits[qtile * 4 + t / 32] >> (t % 32)) & 1u;
   const float inv = (qvalid && l_run > 0.f) ? 1.f / l_run : 0.f;
+  if (lse != nullptr)
+    lse[bh * Lt + qrow] = (qvalid && l_run > 0.f) ? m_run + logf(l_run) : -INFINITY;
   float* dst = op + (bh * Lt + qrow) * D;
 #pragma unroll
   for (int c = 0; c < D; ++c) dst[c] = o[c] * inv;
@@ -745,14 +752,14 @@ __global__ __launch_bounds__(BS) void attn_f32_kernel(
 
 template <int D, int BS>
 void launch_bf16(const rf_plan* p, const void* qp, const void* kp,
-                 const void* vt, const int32_t* kept, void* op, int BH,
+                 const void* vt, const int32_t* kept, void* op, float* lse, int BH,
                  int32_t row_len_video, int64_t nnz, float scale, hipStream_t st) {
   const int nb = p->sz.nb, n_tt = p->sz.n_text_tiles;
   dim3 grid(BH * (nb + n_tt));
   if constexpr (BS == 128) {
     hipLaunchKernelGGL((attn_bf16_pp_kernel<D>), grid, dim3(PpCfg<D>::kThreads), 0, st,
                        static_cast<const __bf16*>(qp), static_cast<const __bf16*>(kp),
-                       static_cast<const __bf16*>(vt), kept, static_cast<__bf16*>(op),
+                       static_cast<const __bf16*>(vt), kept, static_cast<__bf16*>(op), lse,
                        p->tile_bits, p->tile_count, p->sz.Lt, BH, nb, n_tt,
                        row_len_video, nnz,
                        scale * 1.4426950408889634f);
@@ -761,7 +768,7 @@ void launch_bf16(const rf_plan* p, const void* qp, const void* kp,
   hipLaunchKernelGGL((attn_bf16_kernel<D, BS>), grid,
                      dim3(Bf16Cfg<D, BS>::kThreads), 0, st,
                      static_cast<const __bf16*>(qp), static_cast<const __bf16*>(kp),
-                     static_cast<const __bf16*>(vt), kept, static_cast<__bf16*>(op),
+                     static_cast<const __bf16*>(vt), kept, static_cast<__bf16*>(op), lse,
                      p->tile_bits, p->tile_count, p->sz.Lt, BH, nb, n_tt,
                      row_len_video, nnz,
                      scale * 1.4426950408889634f);
@@ -769,13 +776,13 @@ void launch_bf16(const rf_plan* p, const void* qp, const void* kp,
 
 template <int D, int BS>
 void launch_f32(const rf_plan* p, const void* qp, const void* kp,
-                const void* vt, const int32_t* kept, void* op, int BH,
+                const void* vt, const int32_t* kept, void* op, float* lse, int BH,
                 int32_t row_len_video, int64_t nnz, float scale, hipStream_t st) {
   const int nb = p->sz.nb, n_tt = p->sz.n_text_tiles;
   dim3 grid(BH * (nb + n_tt));
   hipLaunchKernelGGL((attn_f32_kernel<D, BS>), grid, dim3(BS), 0, st,
                      static_cast<const float*>(qp), static_cast<const float*>(kp),
-                     static_cast<const float*>(vt), kept, static_cast<float*>(op),
+                     static_cast<const float*>(vt), kept, static_cast<float*>(op), lse,
                      p->tile_bits, p->tile_count, p->sz.Lt, BH, nb, n_tt,
                      row_len_video, nnz, scale);
 }
@@ -784,7 +791,7 @@ void launch_f32(const rf_plan* p, const void* qp, const void* kp,
 // layout, row_len_video = -width the padded-row layout.
 rf_status sparse_attn(const rf_plan* plan, const void* qp, const void* kp,
                       const void* vt, const int32_t* kept_idx,
-                      int32_t row_len_video, int64_t nnz, void* op, int32_t B,
+                      int32_t row_len_video, int64_t nnz, void* op, float* lse, int32_t B,
                       int32_t H, int32_t d, float scale, rf_dtype dtype,
                       hipStream_t stream, const char* fn) {
   rf_status st = rf::check_call(plan, B, H, d, dtype, fn);
@@ -792,6 +799,8 @@ rf_status sparse_attn(const rf_plan* plan, const void* qp, const void* kp,
   if (!rf::aligned16(qp) || !rf::aligned16(kp) || !rf::aligned16(vt) ||
       !rf::aligned16(kept_idx) || !rf::aligned16(op))
     return rf::fail(RF_ERR_INVALID_ARG, "%s: null or misaligned buffer", fn);
+  if (reinterpret_cast<uintptr_t>(lse) & 3u)
+    return rf::fail(RF_ERR_INVALID_ARG, "%s: misaligned lse", fn);
   if (!(scale > 0.f) || !(scale < 1e30f))
     return rf::fail(RF_ERR_INVALID_ARG, "%s: scale must be positive and finite", fn);
   const int BH = B * H;
@@ -800,15 +809,15 @@ rf_status sparse_attn(const rf_plan* plan, const void* qp, const void* kp,
   const int bs = plan->sz.bs;
   const int32_t rl = row_len_video;
   if (dtype == RF_BF16) {
-    if (d == 128 && bs == 128) launch_bf16<128, 128>(plan, qp, kp, vt, kept_idx, op, BH, rl, nnz, scale, stream);
-    else if (d == 128 && bs == 64) launch_bf16<128, 64>(plan, qp, kp, vt, kept_idx, op, BH, rl, nnz, scale, stream);
-    else if (d == 64 && bs == 128) launch_bf16<64, 128>(plan, qp, kp, vt, kept_idx, op, BH, rl, nnz, scale, stream);
-    else launch_bf16<64, 64>(plan, qp, kp, vt, kept_idx, op, BH, rl, nnz, scale, stream);
+    if (d == 128 && bs == 128) launch_bf16<128, 128>(plan, qp, kp, vt, kept_idx, op, lse, BH, rl, nnz, scale, stream);
+    else if (d == 128 && bs == 64) launch_bf16<128, 64>(plan, qp, kp, vt, kept_idx, op, lse, BH, rl, nnz, scale, stream);
+    else if (d == 64 && bs == 128) launch_bf16<64, 128>(plan, qp, kp, vt, kept_idx, op, lse, BH, rl, nnz, scale, stream);
+    else launch_bf16<64, 64>(plan, qp, kp, vt, kept_idx, op, lse, BH, rl, nnz, scale, stream);
   } else {
-    if (d == 128 && bs == 128) launch_f32<128, 128>(plan, qp, kp, vt, kept_idx, op, BH, rl, nnz, scale, stream);
-    else if (d == 128 && bs == 64) launch_f32<128, 64>(plan, qp, kp, vt, kept_idx, op, BH, rl, nnz, scale, stream);
-    else if (d == 64 && bs == 128) launch_f32<64, 128>(plan, qp, kp, vt, kept_idx, op, BH, rl, nnz, scale, stream);
-    else launch_f32<64, 64>(plan, qp, kp, vt, kept_idx, op, BH, rl, nnz, scale, stream);
+    if (d == 128 && bs == 128) launch_f32<128, 128>(plan, qp, kp, vt, kept_idx, op, lse, BH, rl, nnz, scale, stream);
+    else if (d == 128 && bs == 64) launch_f32<128, 64>(plan, qp, kp, vt, kept_idx, op, lse, BH, rl, nnz, scale, stream);
+    else if (d == 64 && bs == 128) launch_f32<64, 128>(plan, qp, kp, vt, kept_idx, op, lse, BH, rl, nnz, scale, stream);
+    else launch_f32<64, 64>(plan, qp, kp, vt, kept_idx, op, lse, BH, rl, nnz, scale, stream);
   }
   return rf::check_launch(fn);
 }
@@ -818,28 +827,30 @@ rf_status sparse_attn(const rf_plan* plan, const void* qp, const void* kp,
 extern "C" rf_status rf_sparse_attn(const rf_plan* plan, const void* qp,
                                     const void* kp, const void* vt,
                                     const int32_t* kept_idx,
-                                    int32_t sparsity_pct, void* op, int32_t B,
-                                    int32_t H, int32_t d, float scale,
-                                    rf_dtype dtype, hipStream_t stream) {
+                                    int32_t sparsity_pct, void* op,
+                                    float* lse_or_null, int32_t B, int32_t H,
+                                    int32_t d, float scale, rf_dtype dtype,
+                                    hipStream_t stream) {
   if (plan == nullptr) return rf::fail(RF_ERR_INVALID_ARG, "rf_sparse_attn: null plan");
   rf_keep kc;
   rf_status st = rf_keep_count(&plan->lay, sparsity_pct, &kc);
   if (st != RF_OK) return st;
   return sparse_attn(plan, qp, kp, vt, kept_idx, kc.row_len_video, kc.nnz_per_head,
-                     op, B, H, d, scale, dtype, stream, "rf_sparse_attn");
+                     op, lse_or_null, B, H, d, scale, dtype, stream, "rf_sparse_attn");
 }
 
 extern "C" rf_status rf_sparse_attn_rows(const rf_plan* plan, const void* qp,
                                          const void* kp, const void* vt,
                                          const int32_t* kept_rows,
-                                         int32_t row_width, void* op, int32_t B,
-                                         int32_t H, int32_t d, float scale,
-                                         rf_dtype dtype, hipStream_t stream) {
+                                         int32_t row_width, void* op,
+                                         float* lse_or_null, int32_t B, int32_t H,
+                                         int32_t d, float scale, rf_dtype dtype,
+                                         hipStream_t stream) {
   if (plan == nullptr) return rf::fail(RF_ERR_INVALID_ARG, "rf_sparse_attn_rows: null plan");
   if (row_width < 1 || row_width > plan->sz.n_tiles)
     return rf::fail(RF_ERR_INVALID_ARG, "rf_sparse_attn_rows: row_width %d outside [1, %d]",
                     row_width, plan->sz.n_tiles);
   return sparse_attn(plan, qp, kp, vt, kept_rows, -row_width,
-                     int64_t(plan->sz.n_tiles) * row_width, op, B, H, d, scale,
-                     dtype, stream, "rf_sparse_attn_rows");
+                     int64_t(plan->sz.n_tiles) * row_width, op, lse_or_null, B, H, d,
+                     scale, dtype, stream, "rf_sparse_attn_rows");
 }

@@ -26,8 +26,9 @@
 //   * logits are dot(q8, k8) * scale * 2^(eq + ek) (the key tile's scale
 //     enters the exp2 multiplier), and the feature scales of V multiply the
 //     output once at the end.
-// Weights are exp2(l - m) <= 2^8 under the lazy rescale (threshold 8), inside
-// the e4m3 range (448).
+// Weights are exp2(l - m + 4) <= 2^8 under a lazy rescale with threshold 4,
+// inside the e4m3 range (448), with weights down to 2^-10 of the row maximum
+// still normal e4m3 numbers.
 #include "rf_internal.h"
 #include "tile_common.h"
 
@@ -47,6 +48,15 @@ constexpr int kRowBytes = 128;                  // K row (D fp8) and V^T row (BS
 constexpr int kTileBytes = BS * D;              // 16 KB
 constexpr int kCopies = kTileBytes / 16 / (kGroupWaves * 64);   // 4 per thread
 static_assert(kCopies == 4, "copy split");
+// Softmax weights: rescale threshold and exponent shift (log2 units); their
+// sum bounds every weight by 2^8, within e4m3's largest finite value.
+// A smaller threshold allows a larger shift (finer small weights) but makes
+// rescales more frequent: 8/0 -> 4/4 costs about 1.5% of the kernel's time at
+// 720p / 80% sparsity and cuts the error of the weight sum about tenfold on
+// wide logit distributions.
+constexpr float kRescale = 4.f;
+constexpr float kShift = 4.f;
+static_assert(kRescale + kShift <= 8.f, "weights must stay within e4m3");
 
 __device__ inline f32x16 mma(const i32x8& a, const i32x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
@@ -70,7 +80,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
     const uint8_t* __restrict__ k8, const float* __restrict__ k_scale,
     const uint8_t* __restrict__ v8, const float* __restrict__ v_scale,
-    const int32_t* __restrict__ kept, __bf16* __restrict__ op,
+    const int32_t* __restrict__ kept, __bf16* __restrict__ op, float* __restrict__ lse,
     const uint32_t* __restrict__ tile_bits, const int32_t* __restrict__ tile_count,
     int64_t Lt, int32_t BH, int32_t nb, int32_t n_tt, int32_t row_len_video, int64_t nnz,
     float scale_log2) {
@@ -222,9 +232,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
     // Pad keys have all-zero K rows, so their scores are exactly 0, and
     // all-zero V^T columns, so their weights add nothing to O; the row sum
     // counts valid keys only.  When every query's tile maximum is positive it
-    // comes from a valid key, and a pad weight 2^(0 - m) stays within 2^8, so
-    // the pads need no mask.  Otherwise (and for a masked tile, kt < 0, whose
-    // copies hold tile 0) they are set to -inf.
+    // comes from a valid key, and a pad weight 2^(0 - m + kShift) stays below
+    // 2^(kRescale + kShift) = 2^8 (see below), so the pads need no mask.
+    // Otherwise (and for a masked tile, kt < 0, whose copies hold tile 0)
+    // they are set to -inf.
     if (tcount != BS && (kt < 0 || __ballot(!(mx > 0.f)) != 0)) {
       // Register r of block kb in lane group g is key 64(kb/2) + 32g +
       // 16(kb%2) + r: validity word 2(kb/2) + g, bit 16(kb%2) + r.
@@ -240,8 +251,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
       }
       mx = row_max();
     }
+    // Weights are 2^(logit - m + kShift), m the running maximum, which only
+    // moves (rescaling O and l) when some query's tile maximum exceeds it by
+    // more than kRescale: every weight then stays within 2^8 (e4m3 holds up
+    // to 448), and the shift puts weights down to 2^-10 of the maximum in the
+    // normal e4m3 range instead of leaving them to the subnormal steps.
     const float mt = mx * c;
-    if (__ballot(mt > m_run + 8.f) != 0) {
+    if (__ballot(mt > m_run + kRescale) != 0) {
       const float m_new = fmaxf(m_run, mt);
       const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
@@ -249,7 +265,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
     }
-    const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+    const float neg_m = m_run == -INFINITY ? 0.f : kShift - m_run;
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -310,6 +326,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
   const bool qvalid = (tile_bits[qtile * 4 + qs / 32] >> (qs % 32)) & 1u;
   const float inv = (qvalid && l_tot > 0.f) ? 1.f / l_tot : 0.f;
   const float ca = fa * inv, cb = fb * inv;
+  if (lse != nullptr && g == 0) lse[bh * Lt + qrow] = lse_of(m_t - kShift, l_tot, qvalid);
   // Lane (li, g) holds O^T[dd = db*32 + 8a + 4g + b][query li].
   __bf16* dst = op + (bh * Lt + qrow) * D + 4 * g;
   const float* vsc = v_scale + bh * D + 4 * g;
@@ -333,7 +350,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
 rf_status attn_fp8(const rf_plan* plan, const void* q8, const float* q_scale, const void* k8,
                    const float* k_scale, const void* v8, const float* v_scale,
                    const int32_t* kept, int32_t row_len_video, int64_t nnz, void* op,
-                   int32_t B, int32_t H, int32_t d, float scale, hipStream_t stream,
+                   float* lse, int32_t B, int32_t H, int32_t d, float scale, hipStream_t stream,
                    const char* fn) {
   rf_status st = rf::check_call(plan, B, H, d, RF_BF16, fn);
   if (st != RF_OK) return st;
@@ -344,6 +361,8 @@ rf_status attn_fp8(const rf_plan* plan, const void* q8, const float* q_scale, co
       q_scale == nullptr || k_scale == nullptr ||
       (reinterpret_cast<uintptr_t>(q_scale) & 3u) || (reinterpret_cast<uintptr_t>(k_scale) & 3u))
     return rf::fail(RF_ERR_INVALID_ARG, "%s: null or misaligned buffer", fn);
+  if (reinterpret_cast<uintptr_t>(lse) & 3u)
+    return rf::fail(RF_ERR_INVALID_ARG, "%s: misaligned lse", fn);
   if (!(scale > 0.f) || !(scale < 1e30f))
     return rf::fail(RF_ERR_INVALID_ARG, "%s: scale must be positive and finite", fn);
   const int BH = B * H;
@@ -353,7 +372,7 @@ rf_status attn_fp8(const rf_plan* plan, const void* q8, const float* q_scale, co
   hipLaunchKernelGGL(attn_fp8_pp_kernel, dim3(BH * (nb + n_tt)), dim3(kThreads), 0, stream,
                      static_cast<const uint8_t*>(q8), q_scale, static_cast<const uint8_t*>(k8),
                      k_scale, static_cast<const uint8_t*>(v8), v_scale, kept,
-                     static_cast<__bf16*>(op), plan->tile_bits, plan->tile_count,
+                     static_cast<__bf16*>(op), lse, plan->tile_bits, plan->tile_count,
                      plan->sz.Lt, BH, nb, n_tt, row_len_video, nnz,
                      scale * 1.4426950408889634f);
   return rf::check_launch(fn);
@@ -365,29 +384,32 @@ extern "C" rf_status rf_sparse_attn_fp8(const rf_plan* plan, const void* q8,
                                         const float* q_scale, const void* k8,
                                         const float* k_scale, const void* v8,
                                         const float* v_scale, const int32_t* kept_idx,
-                                        int32_t sparsity_pct, void* op, int32_t B, int32_t H,
-                                        int32_t d, float scale, hipStream_t stream) {
+                                        int32_t sparsity_pct, void* op, float* lse_or_null,
+                                        int32_t B, int32_t H, int32_t d, float scale,
+                                        hipStream_t stream) {
   if (plan == nullptr) return rf::fail(RF_ERR_INVALID_ARG, "rf_sparse_attn_fp8: null plan");
   rf_keep kc;
   rf_status st = rf_keep_count(&plan->lay, sparsity_pct, &kc);
   if (st != RF_OK) return st;
   return attn_fp8(plan, q8, q_scale, k8, k_scale, v8, v_scale, kept_idx, kc.row_len_video,
-                  kc.nnz_per_head, op, B, H, d, scale, stream, "rf_sparse_attn_fp8");
+                  kc.nnz_per_head, op, lse_or_null, B, H, d, scale, stream,
+                  "rf_sparse_attn_fp8");
 }
 
 extern "C" rf_status rf_sparse_attn_fp8_rows(const rf_plan* plan, const void* q8,
                                              const float* q_scale, const void* k8,
                                              const float* k_scale, const void* v8,
                                              const float* v_scale, const int32_t* kept_rows,
-                                             int32_t row_width, void* op, int32_t B,
-                                             int32_t H, int32_t d, float scale,
-                                             hipStream_t stream) {
+                                             int32_t row_width, void* op,
+                                             float* lse_or_null, int32_t B, int32_t H,
+                                             int32_t d, float scale, hipStream_t stream) {
   if (plan == nullptr)
     return rf::fail(RF_ERR_INVALID_ARG, "rf_sparse_attn_fp8_rows: null plan");
   if (row_width < 1 || row_width > plan->sz.n_tiles)
     return rf::fail(RF_ERR_INVALID_ARG, "rf_sparse_attn_fp8_rows: row_width %d outside [1, %d]",
                     row_width, plan->sz.n_tiles);
   return attn_fp8(plan, q8, q_scale, k8, k_scale, v8, v_scale, kept_rows, -row_width,
-                  int64_t(plan->sz.n_tiles) * row_width, op, B, H, d, scale, stream,
+                  int64_t(plan->sz.n_tiles) * row_width, op, lse_or_null, B, H, d, scale,
+                  stream,
                   "rf_sparse_attn_fp8_rows");
 }

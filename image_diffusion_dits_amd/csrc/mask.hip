@@ -249,6 +249,25 @@ __global__ void text_rows_kernel(int32_t* __restrict__ kept, int32_t nb,
   for (int t = threadIdx.x; t < n_tiles; t += blockDim.x) out[t] = t;
 }
 
+// Dense copy of the kept sets, one workgroup per (query tile, head): the
+// row is cleared, then each kept entry sets its byte.
+__global__ void dense_mask_kernel(const int32_t* __restrict__ kept,
+                                  uint8_t* __restrict__ mask, int32_t nb,
+                                  int32_t n_tiles, int32_t row_len_video,
+                                  int64_t nnz) {
+  const int64_t bh = blockIdx.y;
+  const int32_t tile = blockIdx.x;
+  const rf::RowRef rr = rf::row_ref(kept + bh * nnz, tile, nb, row_len_video, n_tiles);
+  const int32_t* row = kept + bh * nnz + rr.offset;
+  uint8_t* dst = mask + (bh * n_tiles + tile) * int64_t(n_tiles);
+  for (int t = threadIdx.x; t < n_tiles; t += blockDim.x) dst[t] = 0;
+  __syncthreads();
+  for (int j = threadIdx.x; j < rr.len; j += blockDim.x) {
+    const int32_t t = row[j];
+    if (t >= 0 && t < n_tiles) dst[t] = 1;
+  }
+}
+
 template <int D, int MMAX>
 void launch_mfma(const rf_plan* p, const float* qbar, const float* kbar,
                  int32_t* kept, float* logits, int BH, const rf_keep& kc,
@@ -297,8 +316,8 @@ void launch(const rf_plan* p, const float* qbar, const float* kbar,
 extern "C" rf_status rf_predict_mask(const rf_plan* plan, const float* qbar,
                                      const float* kbar, int32_t B, int32_t H,
                                      int32_t d, int32_t sparsity_pct,
-                                     int32_t* kept_idx, float* logits_or_null,
-                                     hipStream_t stream) {
+                                     int32_t* kept_idx, uint8_t* mask_or_null,
+                                     float* logits_or_null, hipStream_t stream) {
   rf_status st = rf::check_call(plan, B, H, d, RF_F32, "rf_predict_mask");
   if (st != RF_OK) return st;
   if (!rf::aligned16(qbar) || !rf::aligned16(kbar) || !rf::aligned16(kept_idx))
@@ -328,6 +347,12 @@ extern "C" rf_status rf_predict_mask(const rf_plan* plan, const float* qbar,
     dim3 grid(plan->sz.n_text_tiles, BH);
     hipLaunchKernelGGL(text_rows_kernel, grid, dim3(256), 0, stream, kept_idx,
                        nb, plan->sz.n_tiles, kc.row_len_video, kc.nnz_per_head);
+  }
+  if (mask_or_null != nullptr) {
+    dim3 grid(plan->sz.n_tiles, BH);
+    hipLaunchKernelGGL(dense_mask_kernel, grid, dim3(256), 0, stream, kept_idx,
+                       mask_or_null, nb, plan->sz.n_tiles, kc.row_len_video,
+                       kc.nnz_per_head);
   }
   return rf::check_launch("rf_predict_mask");
 }

@@ -98,4 +98,12 @@ __device__ __forceinline__ void dma_tile_perm(const char* base, int bytes, void*
         soff[u], 0, 0);
 }
 
+// Natural-log softmax normaliser of one query from the reference maximum m
+// (log2 units of the scaled logits) and the weight sum l taken relative to
+// it: ln sum_j exp(logit_j) = (m + log2 l) ln 2.  -inf for a pad query or a
+// query that saw no valid key.
+__device__ inline float lse_of(float m, float l, bool valid) {
+  return (valid && l > 0.f) ? (m + log2f(l)) * 0.69314718055994531f : -INFINITY;
+}
+
 }  // namespace rf_tile

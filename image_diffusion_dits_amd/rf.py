@@ -67,15 +67,15 @@ _SIGNATURES = {
     "rf_block_means": [_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32,
                        ctypes.c_int, _vp],
     "rf_predict_mask": [_vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _vp,
-                        _vp, _vp],
-    "rf_sparse_attn": [_vp, _vp, _vp, _vp, _vp, _c_i32, _vp, _c_i32, _c_i32,
-                       _c_i32, _c_f32, ctypes.c_int, _vp],
+                        _vp, _vp, _vp],
+    "rf_sparse_attn": [_vp, _vp, _vp, _vp, _vp, _c_i32, _vp, _vp, _c_i32,
+                       _c_i32, _c_i32, _c_f32, ctypes.c_int, _vp],
     "rf_attention_recall": [_vp, _vp, _vp, _vp, _c_i32, _vp, _c_i32, _c_i32,
                             _c_i32, _c_i32, _c_f32, ctypes.c_int, _vp, _vp],
     "rf_tile_rank": [_P(Layout), _vp, _c_i64],
     "rf_pattern_row_width": [_P(Layout), _c_i32, _c_i32, _P(_c_i32)],
     "rf_arm_sample_count": [_P(Layout), _c_i32, _c_i32, _P(_c_i32)],
-    "rf_sparse_attn_rows": [_vp, _vp, _vp, _vp, _vp, _c_i32, _vp, _c_i32,
+    "rf_sparse_attn_rows": [_vp, _vp, _vp, _vp, _vp, _c_i32, _vp, _vp, _c_i32,
                             _c_i32, _c_i32, _c_f32, ctypes.c_int, _vp],
     "rf_attention_recall_rows": [_vp, _vp, _vp, _vp, _c_i32, _vp, _c_i32,
                                  _c_i32, _c_i32, _c_i32, _c_f32, ctypes.c_int,
@@ -91,9 +91,9 @@ _SIGNATURES = {
     "rf_permute_fp8": [_vp, _vp, ctypes.c_int, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32,
                        ctypes.c_int, _vp],
     "rf_sparse_attn_fp8": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _vp,
-                           _c_i32, _c_i32, _c_i32, _c_f32, _vp],
+                           _vp, _c_i32, _c_i32, _c_i32, _c_f32, _vp],
     "rf_sparse_attn_fp8_rows": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i32,
-                                _vp, _c_i32, _c_i32, _c_i32, _c_f32, _vp],
+                                _vp, _vp, _c_i32, _c_i32, _c_i32, _c_f32, _vp],
 }
 
 _lib = None
@@ -310,34 +310,54 @@ def block_means(plan, qp, kp, qbar=None, kbar=None):
     return qbar, kbar
 
 
-def predict_mask(plan, qbar, kbar, sparsity_pct, kept=None, logits=False):
+def predict_mask(plan, qbar, kbar, sparsity_pct, kept=None, logits=False,
+                 dense=False):
+    """Kept tiles [B, H, nnz_per_head]; with logits=True also the fp32 block
+    logits [B, H, nb, nb], with dense=True also the uint8 tile mask
+    [B, H, n_tiles, n_tiles], returned in that order after kept."""
     B, H, d = _bhd(qbar)
     kc = plan.keep(sparsity_pct)
     if kept is None:
         kept = torch.empty(B, H, kc["nnz_per_head"], dtype=torch.int32,
                            device=qbar.device)
-    lg = None
+    lg = mask = None
     if logits:
         nb = plan.sizes["nb"]
         lg = torch.empty(B, H, nb, nb, dtype=torch.float32, device=qbar.device)
+    if dense:
+        nt = plan.sizes["n_tiles"]
+        mask = torch.empty(B, H, nt, nt, dtype=torch.uint8, device=qbar.device)
     _check(lib().rf_predict_mask(plan.handle, _ptr(qbar), _ptr(kbar), B, H, d,
                                  int(sparsity_pct), _ptr(kept),
-                                 _ptr(lg) if lg is not None else None,
+                                 _ptr(mask) if dense else None,
+                                 _ptr(lg) if logits else None,
                                  _stream()), "rf_predict_mask")
-    return (kept, lg) if logits else kept
+    extra = ([lg] if logits else []) + ([mask] if dense else [])
+    return (kept, *extra) if extra else kept
 
 
-def sparse_attn(plan, qp, kp, vt, kept, sparsity_pct, scale=None, out=None):
+def _lse_out(want, qp):
+    if not want:
+        return None
+    B, H, Lt = qp.shape[:3]
+    return torch.empty(B, H, Lt, dtype=torch.float32, device=qp.device)
+
+
+def sparse_attn(plan, qp, kp, vt, kept, sparsity_pct, scale=None, out=None,
+                lse=False):
+    """Op [B, H, Lt, d]; with lse=True also the fp32 log-sum-exp [B, H, Lt]."""
     B, H, d = _bhd(qp)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(qp)
+    lo = _lse_out(lse, qp)
     _check(lib().rf_sparse_attn(plan.handle, _ptr(qp), _ptr(kp), _ptr(vt),
-                                _ptr(kept), int(sparsity_pct), _ptr(out), B, H,
+                                _ptr(kept), int(sparsity_pct), _ptr(out),
+                                _ptr(lo) if lse else None, B, H,
                                 d, float(scale), _dtype_code(qp), _stream()),
            "rf_sparse_attn")
-    return out
+    return (out, lo) if lse else out
 
 
 def attention_recall(plan, qp, kp, kept, sparsity_pct, sample_tiles, scale=None,
@@ -361,18 +381,20 @@ def attention_recall(plan, qp, kp, kept, sparsity_pct, sample_tiles, scale=None,
     return out
 
 
-def sparse_attn_rows(plan, qp, kp, vt, rows, scale=None, out=None):
+def sparse_attn_rows(plan, qp, kp, vt, rows, scale=None, out=None, lse=False):
     """rf_sparse_attn on padded kept rows: rows is int32 [B, H, n_tiles, width]."""
     B, H, d = _bhd(qp)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(qp)
+    lo = _lse_out(lse, qp)
     _check(lib().rf_sparse_attn_rows(plan.handle, _ptr(qp), _ptr(kp), _ptr(vt),
-                                     _ptr(rows), rows.shape[-1], _ptr(out), B, H,
+                                     _ptr(rows), rows.shape[-1], _ptr(out),
+                                     _ptr(lo) if lse else None, B, H,
                                      d, float(scale), _dtype_code(qp), _stream()),
            "rf_sparse_attn_rows")
-    return out
+    return (out, lo) if lse else out
 
 
 def attention_recall_rows(plan, qp, kp, rows, sample_tiles, scale=None, out=None):
@@ -493,31 +515,37 @@ def permute_fp8(plan, x, order=ROWS, means=False, out=None, scale=None, xbar=Non
 
 
 def sparse_attn_fp8(plan, q8, qs, k8, ks, v8, vs, kept, sparsity_pct, scale=None,
-                    out=None):
-    """Block-sparse attention on e4m3 operands; bf16 output [B, H, Lt, d]."""
+                    out=None, lse=False):
+    """Block-sparse attention on e4m3 operands; bf16 output [B, H, Lt, d]
+    (and with lse=True the fp32 log-sum-exp [B, H, Lt])."""
     B, H, _, d = q8.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
+    lo = _lse_out(lse, q8)
     _check(lib().rf_sparse_attn_fp8(plan.handle, _ptr(q8), _ptr(qs), _ptr(k8), _ptr(ks),
                                     _ptr(v8), _ptr(vs), _ptr(kept), int(sparsity_pct),
-                                    _ptr(out), B, H, d, float(scale), _stream()),
+                                    _ptr(out), _ptr(lo) if lse else None, B, H, d,
+                                    float(scale), _stream()),
            "rf_sparse_attn_fp8")
-    return out
+    return (out, lo) if lse else out
 
 
-def sparse_attn_fp8_rows(plan, q8, qs, k8, ks, v8, vs, rows, scale=None, out=None):
+def sparse_attn_fp8_rows(plan, q8, qs, k8, ks, v8, vs, rows, scale=None, out=None,
+                         lse=False):
     B, H, _, d = q8.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
+    lo = _lse_out(lse, q8)
     _check(lib().rf_sparse_attn_fp8_rows(plan.handle, _ptr(q8), _ptr(qs), _ptr(k8),
                                          _ptr(ks), _ptr(v8), _ptr(vs), _ptr(rows),
-                                         rows.shape[-1], _ptr(out), B, H, d, float(scale),
+                                         rows.shape[-1], _ptr(out),
+                                         _ptr(lo) if lse else None, B, H, d, float(scale),
                                          _stream()), "rf_sparse_attn_fp8_rows")
-    return out
+    return (out, lo) if lse else out
 
 
 def sparse_attention_fp8(q, k, v, plan, sparsity_pct, scale=None):

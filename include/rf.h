@@ -223,11 +223,16 @@ rf_status rf_block_means(const rf_plan* plan, const void* qp, const void* kp,
  * kept_idx: int32 [B][H][nnz_per_head], rows in tile order, each row
  * ascending (row r of a head starts at r*row_len_video for r < nb and at
  * nb*row_len_video + (r - nb)*row_len_text after that).
- * logits_or_null: optional fp32 [B][H][nb][nb] copy of l. */
+ * mask_or_null: optional uint8 [B][H][n_tiles][n_tiles] dense copy of the
+ * kept sets (1 where row i keeps tile j, else 0), for inspection.
+ * logits_or_null: optional fp32 [B][H][nb][nb] copy of l.  Both optional
+ * outputs are written only when non-null and cost extra writes of their
+ * full size. */
 rf_status rf_predict_mask(const rf_plan* plan, const float* qbar,
                           const float* kbar, int32_t B, int32_t H, int32_t d,
                           int32_t sparsity_pct, int32_t* kept_idx,
-                          float* logits_or_null, hipStream_t stream);
+                          uint8_t* mask_or_null, float* logits_or_null,
+                          hipStream_t stream);
 
 /* Block-sparse attention forward [RF2 Abstract: skipping computations for
  * insignificant tokens; RF1 review, Eq. (1)].  For each valid query slot of
@@ -237,12 +242,17 @@ rf_status rf_predict_mask(const rf_plan* plan, const float* qbar,
  * kept_idx as produced by rf_predict_mask for the same sparsity_pct; every
  * entry must lie in [0, n_tiles).  RF_BF16: bf16 operands, fp32
  * accumulation and softmax, bf16 output; RF_F32: fp32 throughout.
- * d in {64, 128}. */
+ * lse_or_null: optional fp32 [B][H][Lt] (4-byte aligned) receiving each
+ * query's log-sum-exp over its kept keys, ln sum_j exp(scale * q . k_j),
+ * the natural-log softmax normaliser that merges this output with other
+ * partial attentions; -inf at pad query slots and for a query with no
+ * valid kept key.  With RF_BF16 the sum is that of the bf16 weights the
+ * output uses.  d in {64, 128}. */
 rf_status rf_sparse_attn(const rf_plan* plan, const void* qp, const void* kp,
                          const void* vt, const int32_t* kept_idx,
-                         int32_t sparsity_pct, void* op, int32_t B, int32_t H,
-                         int32_t d, float scale, rf_dtype dtype,
-                         hipStream_t stream);
+                         int32_t sparsity_pct, void* op, float* lse_or_null,
+                         int32_t B, int32_t H, int32_t d, float scale,
+                         rf_dtype dtype, hipStream_t stream);
 
 /* Attention-recall diagnostic [RF1 review, "What carries the argument":
  * the masked recall R', attention mass that survives a mask over the mass
@@ -276,8 +286,9 @@ rf_status rf_attention_recall(const rf_plan* plan, const void* qp,
 rf_status rf_sparse_attn_rows(const rf_plan* plan, const void* qp,
                               const void* kp, const void* vt,
                               const int32_t* kept_rows, int32_t row_width,
-                              void* op, int32_t B, int32_t H, int32_t d,
-                              float scale, rf_dtype dtype, hipStream_t stream);
+                              void* op, float* lse_or_null, int32_t B,
+                              int32_t H, int32_t d, float scale, rf_dtype dtype,
+                              hipStream_t stream);
 rf_status rf_attention_recall_rows(const rf_plan* plan, const void* qp,
                                    const void* kp, const int32_t* kept_rows,
                                    int32_t row_width,
@@ -362,17 +373,20 @@ rf_status rf_permute_fp8(const rf_plan* plan, const void* x, rf_order order,
  * [B][H][n_tiles][d][bs] (RF_TILES_T) with per-feature scales v_scale
  * [B][H][d] (16-byte aligned), all from rf_quantize_fp8.  For each valid
  * query slot: o = sum_j w_j (v8_j * v_scale) / sum_j w_j over the valid
- * slots of the kept tiles, w_j = the e4m3 rounding of the softmax weight of
- * logit scale * (q8 . k8_j) * q_scale * k_scale, accumulated in fp32; op
- * bf16 [B][H][Lt][d], pad query rows 0.  kept_idx and sparsity_pct as for
- * rf_sparse_attn.  d = 128 and bs = 128 only (RF_ERR_UNSUPPORTED
- * otherwise). */
+ * slots of the kept tiles, w_j = the e4m3 rounding of 16 exp(x_j - m) for
+ * the logit x_j = scale * (q8 . k8_j) * q_scale * k_scale and a running
+ * reference m at most 4 ln 2 below the row maximum (weights down to 2^-10
+ * of the largest stay normal e4m3 numbers), accumulated in fp32; op bf16
+ * [B][H][Lt][d], pad query rows 0.  kept_idx and sparsity_pct as for
+ * rf_sparse_attn; lse_or_null as for rf_sparse_attn: m - ln 16 +
+ * ln sum_j w_j, the log-sum-exp of the logits with the e4m3 weights.
+ * d = 128 and bs = 128 only (RF_ERR_UNSUPPORTED otherwise). */
 rf_status rf_sparse_attn_fp8(const rf_plan* plan, const void* q8,
                              const float* q_scale, const void* k8,
                              const float* k_scale, const void* v8,
                              const float* v_scale, const int32_t* kept_idx,
-                             int32_t sparsity_pct, void* op, int32_t B,
-                             int32_t H, int32_t d, float scale,
+                             int32_t sparsity_pct, void* op, float* lse_or_null,
+                             int32_t B, int32_t H, int32_t d, float scale,
                              hipStream_t stream);
 
 /* rf_sparse_attn_fp8 on padded kept rows (the layout of
@@ -382,8 +396,9 @@ rf_status rf_sparse_attn_fp8_rows(const rf_plan* plan, const void* q8,
                                   const float* k_scale, const void* v8,
                                   const float* v_scale,
                                   const int32_t* kept_rows, int32_t row_width,
-                                  void* op, int32_t B, int32_t H, int32_t d,
-                                  float scale, hipStream_t stream);
+                                  void* op, float* lse_or_null, int32_t B,
+                                  int32_t H, int32_t d, float scale,
+                                  hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -9,6 +9,14 @@
   attention     bf16: max-abs <= 2e-2 and mean-abs <= 5e-3 over valid rows;
                 fp32: max-abs <= 1e-5.  The oracle row is computed with the
                 GPU's kept list, so a legal borderline swap cannot fail it.
+  log-sum-exp   bf16: |gpu - oracle| <= 4e-3 + 1e-6 |oracle|.  The kernel sums
+                the bf16-rounded weights (8-bit significand: relative error
+                at most 2^-8 each, so the sum is off by at most a factor
+                1 +- 2^-8 and its log by at most -ln(1 - 2^-8) = 3.92e-3);
+                the logits come from fp32 dot products of the same bf16
+                operands the oracle reads.
+                fp32: <= 1e-5 + 1e-6 |oracle|.  Pad slots are -inf on both.
+  dense mask    bit-exact against the kept rows it copies.
 """
 import math
 
@@ -19,6 +27,7 @@ from oracle import rainfusion_oracle as orc
 
 BORDER = 1e-4
 TOL = {"bf16": (2e-2, 5e-3), "f32": (1e-5, 1e-5)}
+LSE_TOL = {"bf16": 4e-3, "f32": 1e-5}
 
 
 def bits(t: torch.Tensor) -> np.ndarray:
@@ -103,3 +112,20 @@ def check_attention(gpu_op: np.ndarray, want_op: np.ndarray, valid: np.ndarray,
     pad = computed & ~valid
     assert np.all(gpu_op[pad] == 0), "pad query rows must be zero"
     return float(err.max()), float(err.mean())
+
+
+def check_lse(gpu_lse: np.ndarray, want_lse: np.ndarray, valid: np.ndarray,
+              dtype: str, tol=None):
+    """gpu_lse, want_lse: [Lp] of one head (want NaN where not computed);
+    tol: optional per-slot bound replacing the dtype's."""
+    computed = ~np.isnan(want_lse)
+    rows = computed & valid
+    assert rows.any()
+    assert np.all(np.isfinite(gpu_lse[rows])), "finite LSE expected at valid slots"
+    err = np.abs(gpu_lse[rows] - want_lse[rows])
+    bound = (LSE_TOL[dtype] if tol is None else tol[rows]) + 1e-6 * np.abs(want_lse[rows])
+    bad = err > bound
+    assert not bad.any(), f"{bad.sum()} LSE values off, worst {err.max():.3e}"
+    pad = computed & ~valid
+    assert np.all(np.isneginf(gpu_lse[pad])), "pad query slots must be -inf"
+    return float(err.max())

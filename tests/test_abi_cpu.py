@@ -129,12 +129,12 @@ def test_gpu_entry_points_reject_bad_arguments_without_a_device():
     assert L.rf_permute(None, buf, buf, 1, 1, 64, rf.BF16, rf.ROWS, None) == rf.ERR_INVALID_ARG
     assert L.rf_unpermute(None, buf, buf, 1, 1, 64, rf.BF16, None) == rf.ERR_INVALID_ARG
     assert L.rf_block_means(None, buf, buf, buf, buf, 1, 1, 64, rf.BF16, None) == rf.ERR_INVALID_ARG
-    assert L.rf_predict_mask(None, buf, buf, 1, 1, 64, 50, buf, None, None) == rf.ERR_INVALID_ARG
-    assert L.rf_sparse_attn(None, buf, buf, buf, buf, 50, buf, 1, 1, 64, 0.125,
+    assert L.rf_predict_mask(None, buf, buf, 1, 1, 64, 50, buf, None, None, None) == rf.ERR_INVALID_ARG
+    assert L.rf_sparse_attn(None, buf, buf, buf, buf, 50, buf, None, 1, 1, 64, 0.125,
                             rf.BF16, None) == rf.ERR_INVALID_ARG
     assert L.rf_attention_recall(None, buf, buf, buf, 50, buf, 1, 1, 1, 64, 0.125,
                                  rf.BF16, buf, None) == rf.ERR_INVALID_ARG
-    assert L.rf_sparse_attn_rows(None, buf, buf, buf, buf, 4, buf, 1, 1, 64, 0.125,
+    assert L.rf_sparse_attn_rows(None, buf, buf, buf, buf, 4, buf, None, 1, 1, 64, 0.125,
                                  rf.BF16, None) == rf.ERR_INVALID_ARG
     assert L.rf_attention_recall_rows(None, buf, buf, buf, 4, buf, 1, 1, 1, 64,
                                       0.125, rf.BF16, buf, None) == rf.ERR_INVALID_ARG
@@ -143,9 +143,9 @@ def test_gpu_entry_points_reject_bad_arguments_without_a_device():
                            rf.BF16, buf, None) == rf.ERR_INVALID_ARG
     assert L.rf_quantize_fp8(None, buf, rf.ROWS, buf, buf, 1, 1, 128, rf.BF16,
                              None) == rf.ERR_INVALID_ARG
-    assert L.rf_sparse_attn_fp8(None, buf, buf, buf, buf, buf, buf, buf, 50, buf, 1, 1,
+    assert L.rf_sparse_attn_fp8(None, buf, buf, buf, buf, buf, buf, buf, 50, buf, None, 1, 1,
                                 128, 0.125, None) == rf.ERR_INVALID_ARG
-    assert L.rf_sparse_attn_fp8_rows(None, buf, buf, buf, buf, buf, buf, buf, 4, buf, 1,
+    assert L.rf_sparse_attn_fp8_rows(None, buf, buf, buf, buf, buf, buf, buf, 4, buf, None, 1,
                                      1, 128, 0.125, None) == rf.ERR_INVALID_ARG
     assert b"null plan" in L.rf_last_error()
     # The classifier needs no plan: its sizes are checked first.

@@ -15,6 +15,14 @@ bf16 rounding of the output (2^-8 |o|) and 2e-3 for fp32 accumulation.
 On inputs whose weights are exact powers of two inside the e4m3 range the
 weights are not rounded at all, and the tolerance is the bf16 one
 (max-abs 1e-2, mean-abs 2e-3).
+
+Log-sum-exp: the kernel's sum is that of the rounded weights.  A weight at
+least 2^-6 of the row maximum is off by at most eps of itself; a smaller one
+by at most min(w, 2^-10) (it rounds to a subnormal step of 2^-9, or to 0),
+so the sum's relative error is at most
+delta = eps + sum_small min(w_j, 2^-10) / sum_j w_j (w_j = 2^(l_j - l_max))
+and the LSE error at most -ln(1 - delta), plus 1e-4 for fp32 logits; -inf
+at pad slots.
 """
 import math
 import sys
@@ -67,16 +75,18 @@ def check_quant(plan, lay, xp_gpu, order, heads=None):
 
 
 def fp8_bound(q8v, k8v, v8v, rows_bh, lay, tiles, scale):
-    """Per-element tolerance of the header for the listed query tiles of one
-    head: dict tile -> [n_rows, d] (NaN rows are pad queries)."""
+    """Per-element tolerances of the header for the listed query tiles of one
+    head: (dict tile -> [n_rows, d] for the output, dict tile -> [n_rows]
+    for the log-sum-exp); NaN rows are pad queries."""
     z = orc.sizes(lay)
     bs, Lp = z["bs"], z["Lp"]
     valid = orc.slot_valid(lay)
     eps = 2.0 ** -4
-    out = {}
+    out, out_lse = {}, {}
     for i in tiles:
         rows = np.arange(i * bs, min((i + 1) * bs, Lp))
         tol = np.full((len(rows), q8v.shape[-1]), np.nan)
+        tol_lse = np.full(len(rows), np.nan)
         qr = rows[valid[rows]]
         keys = np.concatenate([np.arange(j * bs, min((j + 1) * bs, Lp)) for j in rows_bh[i]])
         keys = keys[valid[keys]]
@@ -94,7 +104,12 @@ def fp8_bound(q8v, k8v, v8v, rows_bh, lay, tiles, scale):
             t[a:a + 8] = t1 + t2
         tol[valid[rows]] = t + 2.0 ** -8 * np.abs(o) + 2e-3
         out[i] = tol
-    return out
+        small = np.where(wrel < 2.0 ** -6, np.minimum(wrel, 2.0 ** -10), 0.0)
+        delta = eps + small.sum(axis=1) / wrel.sum(axis=1)
+        assert np.all(delta < 0.5), "LSE bound too loose to test"
+        tol_lse[valid[rows]] = -np.log1p(-delta) + 1e-4
+        out_lse[i] = tol_lse
+    return out, out_lse
 
 
 def run_fp8(plan, q, k, v, s):
@@ -105,9 +120,9 @@ def run_fp8(plan, q, k, v, s):
     q8, qs = rf.quantize_fp8(plan, qp)
     k8, ks = rf.quantize_fp8(plan, kp)
     v8, vs = rf.quantize_fp8(plan, vt, order=rf.TILES_T)
-    op = rf.sparse_attn_fp8(plan, q8, qs, k8, ks, v8, vs, kept, s)
+    op, lse = rf.sparse_attn_fp8(plan, q8, qs, k8, ks, v8, vs, kept, s, lse=True)
     torch.cuda.synchronize()
-    return dict(qp=qp, kp=kp, vt=vt, kept=kept, op=op)
+    return dict(qp=qp, kp=kp, vt=vt, kept=kept, op=op, lse=lse)
 
 
 def check_fp8_attention(lay_dict, q, k, v, s, heads=None, sample_tiles=None, seed=0,
@@ -129,7 +144,9 @@ def check_fp8_attention(lay_dict, q, k, v, s, heads=None, sample_tiles=None, see
     valid = orc.slot_valid(lay)
     rng = np.random.default_rng(seed)
     B, H = q.shape[:2]
-    worst, ratio, errs = 0.0, 0.0, []
+    worst, ratio, errs, lse_worst = 0.0, 0.0, [], 0.0
+    lse = parity.values(g["lse"])
+    assert np.all(np.isneginf(lse[:, :, Lp:])), "LSE of whole-tile pad rows"
     for b in range(B):
         for h in (range(H) if heads is None else heads):
             tiles = (list(range(z["n_tiles"])) if sample_tiles is None else
@@ -143,7 +160,15 @@ def check_fp8_attention(lay_dict, q, k, v, s, heads=None, sample_tiles=None, see
             q8v, _ = orc.quantize_tiles(qv, lay)
             k8v, _ = orc.quantize_tiles(kv, lay)
             v8v, _ = orc.quantize_channels(vv)
-            tol = fp8_bound(q8v[0, 0], k8v[0, 0], v8v[0, 0], rows[b][h], lay, tiles, scale)
+            tol, tol_lse = fp8_bound(q8v[0, 0], k8v[0, 0], v8v[0, 0], rows[b][h], lay,
+                                     tiles, scale)
+            want_lse = orc.attention_lse(q8v, k8v, [[rows[b][h]]], lay, scale=scale,
+                                         query_tiles={(0, 0): tiles})[0, 0]
+            tl = np.full(Lp, np.nan)
+            for i in tiles:
+                tl[i * z["bs"]:min((i + 1) * z["bs"], Lp)] = tol_lse[i]
+            lse_worst = max(lse_worst, parity.check_lse(lse[b, h, :Lp], want_lse, valid,
+                                                        "bf16", tol=tl))
             for i in tiles:
                 sl = slice(i * z["bs"], min((i + 1) * z["bs"], Lp))
                 gi, wi = op[b, h, sl], want[sl]
@@ -158,7 +183,7 @@ def check_fp8_attention(lay_dict, q, k, v, s, heads=None, sample_tiles=None, see
                 errs.append(err.ravel())
     e = np.concatenate(errs)
     say(f"  fp8 attention max_abs={worst:.3e} mean_abs={e.mean():.3e} "
-        f"max err/bound={ratio:.3f}")
+        f"max err/bound={ratio:.3f} lse max_abs={lse_worst:.3e}")
     plan.close()
     return g, e
 
@@ -274,9 +299,10 @@ def test_fp8_rows_matches_predicted_bitwise():
     rows = torch.full((1, 4, z["n_tiles"], kc["row_len_video"] + 1), -1, dtype=torch.int32,
                       device="cuda")
     rows[..., :kc["row_len_video"]] = g["kept"].view(1, 4, z["nb"], kc["row_len_video"])
-    got = rf.sparse_attn_fp8_rows(plan, q8, qs, k8, ks, v8, vs, rows)
+    got, lse = rf.sparse_attn_fp8_rows(plan, q8, qs, k8, ks, v8, vs, rows, lse=True)
     torch.cuda.synchronize()
     assert torch.equal(got, g["op"])
+    assert torch.equal(lse, g["lse"])
     plan.close()
 
 

@@ -27,12 +27,12 @@ def run_gpu(plan, q, k, v, s, logits=False):
     qp, qbar = rf.permute_means(plan, q)
     kp, kbar = rf.permute_means(plan, k)
     vt = rf.permute(plan, v, order=rf.TILES_T)
-    kept, lg = rf.predict_mask(plan, qbar, kbar, s, logits=True)
-    op = rf.sparse_attn(plan, qp, kp, vt, kept, s)
+    kept, lg, dense = rf.predict_mask(plan, qbar, kbar, s, logits=True, dense=True)
+    op, lse = rf.sparse_attn(plan, qp, kp, vt, kept, s, lse=True)
     o = rf.unpermute(plan, op)
     torch.cuda.synchronize()
     return dict(qp=qp, kp=kp, vt=vt, qbar=qbar, kbar=kbar, kept=kept,
-                logits=lg, op=op, o=o)
+                logits=lg, dense=dense, op=op, lse=lse, o=o)
 
 
 def check_case(lay_dict, q, k, v, s, dtype, full_heads=None, sample_tiles=None,
@@ -62,6 +62,10 @@ def check_case(lay_dict, q, k, v, s, dtype, full_heads=None, sample_tiles=None,
     op = parity.values(g["op"][:, :, :Lp])
     for name in ("qp", "kp", "op"):        # whole-tile pad rows after Lp
         assert torch.all(g[name][:, :, Lp:] == 0), name
+    lse = parity.values(g["lse"]) if "lse" in g else None
+    if lse is not None:
+        assert np.all(np.isneginf(lse[:, :, Lp:])), "LSE of whole-tile pad rows"
+    dense = g["dense"].cpu().numpy() if "dense" in g else None
     valid = orc.slot_valid(lay)
     rng = np.random.default_rng(seed)
     stats = dict(swaps=0, max_abs=0.0, mean_abs=[])
@@ -88,6 +92,9 @@ def check_case(lay_dict, q, k, v, s, dtype, full_heads=None, sample_tiles=None,
             kept_o, l = orc.predict_mask(qbo, kbo, lay, s)
             stats["swaps"] += parity.check_mask(rows[b][h], kept_o[0][0],
                                                 l[0, 0], lay, s)
+            if dense is not None:
+                assert np.array_equal(dense[b, h], orc.kept_dense([[rows[b][h]]], lay)[0, 0]), \
+                    f"dense mask b{b} h{h}"
             # attention, with the GPU's kept rows
             if full_heads is None or h in full_heads:
                 tiles = range(z["n_tiles"])
@@ -99,11 +106,17 @@ def check_case(lay_dict, q, k, v, s, dtype, full_heads=None, sample_tiles=None,
                                         [[rows[b][h]]], lay,
                                         query_tiles={(0, 0): tiles})
             mx, mn = parity.check_attention(op[b, h], want[0, 0], valid, dtype)
+            if lse is not None:
+                want_lse = orc.attention_lse(qv, kv, [[rows[b][h]]], lay,
+                                             query_tiles={(0, 0): tiles})
+                stats.setdefault("lse", []).append(
+                    parity.check_lse(lse[b, h, :Lp], want_lse[0, 0], valid, dtype))
             stats["max_abs"] = max(stats["max_abs"], mx)
             stats["mean_abs"].append(mn)
     plan.close()
     say(f"  swaps={stats['swaps']} max_abs={stats['max_abs']:.3e} "
-        f"mean_abs={np.mean(stats['mean_abs']):.3e}")
+        f"mean_abs={np.mean(stats['mean_abs']):.3e} "
+        f"lse_max_abs={max(stats.get('lse', [float('nan')])):.3e}")
     return g, stats
 
 
@@ -199,13 +212,12 @@ def test_repeated_runs_are_bitwise_identical():
     q, k, v = inputs.make_qkv(cfg, "cuda", H=8)
     plan = rf.Plan(cfg.layout)
     outs = [run_gpu(plan, q, k, v, 80) for _ in range(3)]
-    for key in ("qp", "kp", "vt", "qbar", "kbar", "kept", "op", "o"):
-        a = parity.bits(outs[0][key]) if outs[0][key].dtype != torch.int32 \
-            else outs[0][key].cpu().numpy()
+    def host(t):
+        return t.cpu().numpy() if t.dtype in (torch.int32, torch.uint8) else parity.bits(t)
+    for key in ("qp", "kp", "vt", "qbar", "kbar", "kept", "dense", "op", "lse", "o"):
+        a = host(outs[0][key])
         for other in outs[1:]:
-            b = parity.bits(other[key]) if other[key].dtype != torch.int32 \
-                else other[key].cpu().numpy()
-            assert np.array_equal(a, b), key
+            assert np.array_equal(a, host(other[key])), key
     # The sweep's 80% point is the 720p case itself.
     sw = configs.SWEEP
     q2, k2, v2 = inputs.make_qkv(sw, "cuda", H=8)
@@ -261,10 +273,15 @@ def test_gpu_argument_errors():
     assert st == rf.ERR_INVALID_ARG
     kept = torch.zeros(10, dtype=torch.int32, device="cuda")
     st = L.rf_sparse_attn(plan.handle, xp.data_ptr(), xp.data_ptr(), xp.data_ptr(),
-                          kept.data_ptr(), 50, xp.data_ptr(), 1, 2, 64, -1.0,
+                          kept.data_ptr(), 50, xp.data_ptr(), None, 1, 2, 64, -1.0,
                           rf.F32, None)
     assert st == rf.ERR_INVALID_ARG
     st = L.rf_predict_mask(plan.handle, xp.data_ptr(), xp.data_ptr(), 1, 2, 64, 100,
-                           kept.data_ptr(), None, None)
+                           kept.data_ptr(), None, None, None)
     assert st == rf.ERR_INVALID_ARG
+    # A misaligned LSE buffer is refused before any launch.
+    st = L.rf_sparse_attn(plan.handle, xp.data_ptr(), xp.data_ptr(), xp.data_ptr(),
+                          kept.data_ptr(), 50, xp.data_ptr(), xp.data_ptr() + 2, 1, 2,
+                          64, 0.125, rf.F32, None)
+    assert st == rf.ERR_INVALID_ARG and b"lse" in L.rf_last_error()
     plan.close()

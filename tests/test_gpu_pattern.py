@@ -141,20 +141,22 @@ def test_rows_layout_matches_predicted_layout_bitwise():
     kp, kbar = rf.permute_means(plan, k)
     vt = rf.permute(plan, v, order=rf.TILES_T)
     kept = rf.predict_mask(plan, qbar, kbar, s)
-    ref = rf.sparse_attn(plan, qp, kp, vt, kept, s)
+    ref, ref_lse = rf.sparse_attn(plan, qp, kp, vt, kept, s, lse=True)
     kc = plan.keep(s)
     width = kc["row_len_video"] + 3                 # extra -1 padding
     rows = torch.full((1, 8, z["n_tiles"], width), -1, dtype=torch.int32, device="cuda")
     rows[:, :, :, :kc["row_len_video"]] = kept.view(1, 8, z["nb"], kc["row_len_video"])
-    got = rf.sparse_attn_rows(plan, qp, kp, vt, rows)
+    got, got_lse = rf.sparse_attn_rows(plan, qp, kp, vt, rows, lse=True)
     torch.cuda.synchronize()
     assert torch.equal(ref, got)
+    assert torch.equal(ref_lse, got_lse)
     plan.close()
 
 
 @pytest.mark.parametrize("wt", [1, 2], ids=["bs64", "bs128"])
 def test_empty_and_short_rows(wt):
-    """An all -1 row gives zeros; a one-tile row attends to that tile only."""
+    """An all -1 row gives zeros (LSE -inf); a one-tile row attends to that
+    tile only."""
     lay = dict(T=2 * wt, H=8, W=16, wt=wt, wh=8, ww=8, n_text=0, permute=1, sink=0)
     say(f"[rows] empty and one-tile rows, bs={64 * wt}")
     plan = rf.Plan(lay)
@@ -168,18 +170,25 @@ def test_empty_and_short_rows(wt):
         vt = rf.permute(plan, v, order=rf.TILES_T)
         rows = torch.tensor([[[[-1, -1, -1], [2, -1, -1], [0, 1, 3], [1, 3, -1]]]],
                             dtype=torch.int32, device="cuda")
-        op = rf.sparse_attn_rows(plan, qp, kp, vt, rows)
+        op, lse = rf.sparse_attn_rows(plan, qp, kp, vt, rows, lse=True)
         torch.cuda.synchronize()
         Lp = z["Lp"]
         got = parity.values(op)[0, 0]
         assert np.all(got[:bs] == 0)
+        lse = parity.values(lse)[0, 0]
+        assert np.all(np.isneginf(lse[:bs]))
         want = orc.sparse_attention(parity.values(qp[:, :, :Lp]), parity.values(kp[:, :, :Lp]),
                                     orc.permute(parity.values(v), olay),
                                     [[[np.array([0]), np.array([2]), np.array([0, 1, 3]),
                                        np.array([1, 3])]]], olay,
                                     query_tiles={(0, 0): [1, 2, 3]})
-        parity.check_attention(got[:Lp], want[0, 0], orc.slot_valid(olay),
-                               "bf16" if dt == torch.bfloat16 else "f32")
+        dts = "bf16" if dt == torch.bfloat16 else "f32"
+        parity.check_attention(got[:Lp], want[0, 0], orc.slot_valid(olay), dts)
+        want_lse = orc.attention_lse(parity.values(qp[:, :, :Lp]), parity.values(kp[:, :, :Lp]),
+                                     [[[np.array([0]), np.array([2]), np.array([0, 1, 3]),
+                                        np.array([1, 3])]]], olay,
+                                     query_tiles={(0, 0): [1, 2, 3]})
+        parity.check_lse(lse[:Lp], want_lse[0, 0], orc.slot_valid(olay), dts)
     plan.close()
 
 
