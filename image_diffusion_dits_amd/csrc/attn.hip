@@ -384,7 +384,6 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
   constexpr int kWaitVm0 = 0x0F70;     // s_waitcnt vmcnt(0)
   // K and V^T tiles of group 0, then of group 1; reused for the merge.
   __shared__ __align__(16) __bf16 lds[4 * C::kTileElems];
-  __shared__ float m_buf[C::kGroupWaves * 64], l_buf[C::kGroupWaves * 64];
 
   const int32_t n_tiles = nb + n_tt;
   const TileJob job = job_of(blockIdx.x, BH, nb, n_tt);
@@ -396,7 +395,7 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
   const int lane = threadIdx.x % 64;
   const int li = lane % 32, g = lane / 32;
   __bf16* const ks = lds + (2 * grp) * C::kTileElems;
-  __bf16* const vs = lds + (2 * grp + 1) * C::kTileElems;
+  __bf16* const vsg = lds + (2 * grp + 1) * C::kTileElems;
 
   const char* kh = reinterpret_cast<const char*>(kp + bh * Lt * D);
   const char* vh = reinterpret_cast<const char*>(vt + bh * int64_t(n_tiles) * D * BS);
@@ -435,10 +434,6 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
     dma_tile<C::kCopies, C::kGroupWaves>(kh + int64_t(max(kt, 0)) * C::kTileBytes,
                                          C::kTileBytes, ks, koff, qw);
   };
-  auto copy_v = [&](int32_t kt) {
-    dma_tile<C::kCopies, C::kGroupWaves>(vh + int64_t(max(kt, 0)) * C::kTileBytes,
-                                         C::kTileBytes, vs, voff, qw);
-  };
 
   // LDS element offsets of this lane's operand chunks.
   //   K (A of S^T): row kb*32 + sigma(li), chunk 2m + g.
@@ -464,6 +459,16 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
 
   // MFMA phase of tile i.
   auto mfma_phase = [&](int32_t i) {
+    // The lane parts of the operand addresses pass through an empty asm at
+    // each phase, so the swizzled addresses are derived here (a few VALU
+    // instructions beside the MFMAs) instead of all being held in registers
+    // across the softmax.  Chunk c of a row sits at chunk c ^ swz(row); for
+    // even c0, (c0 + g) ^ swz = c0 ^ (g ^ swz).
+    int vlane = li * C::kVRowBytes, vx = (g ^ vswz) * 16;
+    int klane = krow0 * C::kKRowBytes, kx = (g ^ kswz) * 16;
+    asm volatile("" : "+v"(vlane), "+v"(vx), "+v"(klane), "+v"(kx));
+    const char* const vs = reinterpret_cast<const char*>(vsg) + vlane;
+    const char* const kq = reinterpret_cast<const char*>(ks) + klane;
     if (i >= 1) {
       // O^T[db] += V^T[db rows, keys] P^T(i-1); MFMA (kb, h) takes keys
       // kb*32 + 16h + 8g .. +8 in lane group g.
@@ -471,11 +476,11 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
       for (int kb = 0; kb < BS / 32; ++kb) {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const __bf16* va = vs + (db * 32 + li) * BS;
+          const char* va = vs + db * 32 * C::kVRowBytes;
 #pragma unroll
           for (int h = 0; h < 2; ++h)
             o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                *reinterpret_cast<const bf16x8*>(va + ((4 * kb + 2 * h + g) ^ vswz) * 8),
+                *reinterpret_cast<const bf16x8*>(va + (((4 * kb + 2 * h) * 16) ^ vx)),
                 pb[kb][h], o[db], 0, 0, 0);
         }
       }
@@ -493,24 +498,43 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
 #pragma unroll
       for (int kb = 0; kb < BS / 32; ++kb) {
         s[kb] = f32x16{};
-        const __bf16* ka = ks + (kb * 32 + krow0) * D;
+        const char* ka = kq + kb * 32 * C::kKRowBytes;
 #pragma unroll
         for (int m = 0; m < D / 16; ++m)
           s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              *reinterpret_cast<const bf16x8*>(ka + ((2 * m + g) ^ kswz) * 8), qf[m],
+              *reinterpret_cast<const bf16x8*>(ka + ((2 * m * 16) ^ kx)), qf[m],
               s[kb], 0, 0, 0);
       }
       pipeline_reads();
     }
   };
 
-  // VALU phase of tile i: start the copies of K(i+1) and V^T(i) (their
-  // buffers were last read in the MFMA phase just finished), then softmax(i).
+  // VALU phase of tile i: the copies of K(i+1) and V^T(i) (their buffers
+  // were last read in the MFMA phase just finished) and softmax(i).
   auto valu_phase = [&](int32_t i) {
     if (i < 0 || i >= n_grp) return;
     const int32_t kt = tile_of(i);
-    if (i + 1 < n_grp) copy_k(tile_of(i + 1));
-    copy_v(kt);
+    const bool next_k = i + 1 < n_grp;
+    const TileCopy<C::kGroupWaves> ck(kh + int64_t(max(next_k ? tile_of(i + 1) : 0, 0)) *
+                                          C::kTileBytes, C::kTileBytes, ks, koff, qw);
+    const TileCopy<C::kGroupWaves> cv(vh + int64_t(max(kt, 0)) * C::kTileBytes, C::kTileBytes,
+                                      vsg, voff, qw);
+    static_assert(C::kCopies <= 8, "copy schedule below");
+    // Copies u of K(i+1) and V^T(i), each pair followed by a barrier to the
+    // scheduler so that the pairs stay spread through the softmax (a wave
+    // stalls at a copy while the memory pipeline is full, so a burst would
+    // hold back the arithmetic behind it).
+    auto copies = [&](auto u) {
+      constexpr int U = decltype(u)::value;
+      if constexpr (U < C::kCopies) {
+        if (next_k) ck.template issue<U>();
+        cv.template issue<U>();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    copies(I0{});
     const int32_t tcount = kt >= 0 ? tile_count[kt] : 0;
     // Row max over the tile (raw dot products; the scale is positive).
     auto row_max = [&]() {
@@ -524,6 +548,7 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
       return fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));   // max with lane ^ 32
     };
     float mx = row_max();
+    copies(I1{});
     // Pad keys have all-zero K rows, so they score exactly 0, and all-zero
     // V^T columns, so their weights add nothing to O.  When every query's
     // tile maximum is positive it comes from a valid key and a pad weight
@@ -563,34 +588,48 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
       for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
     }
     const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+    // Row sum of the fp32 weights by plain adds, a tree per eight (a chain
+    // of dot-product instructions over the bf16 weights is several times
+    // slower while the other wave of the SIMD issues MFMAs).
     float lsum = l_run;
+    auto weights = [&](auto kbh) {
+      constexpr int kb = decltype(kbh)::value / 2, h = decltype(kbh)::value % 2;
+      f32x8 p;
 #pragma unroll
-    for (int kb = 0; kb < BS / 32; ++kb) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        f32x8 p;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          p[e] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * h + e], scale_log2, neg_m));
-        pb[kb][h] = __builtin_convertvector(p, bf16x8);
-        // Row sum of the bf16 weights the MFMA uses.
-        const bf16x8 w = pb[kb][h];
-        const bf16x2 one = {__bf16(1.f), __bf16(1.f)};
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 0, 1), one, lsum, false);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 2, 3), one, lsum, false);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 4, 5), one, lsum, false);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 6, 7), one, lsum, false);
-      }
-    }
+      for (int e = 0; e < 8; ++e)
+        p[e] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * h + e], scale_log2, neg_m));
+      pb[kb][h] = __builtin_convertvector(p, bf16x8);
+      lsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      // Pure arithmetic may otherwise be moved across the copies: the empty
+      // asm (ordered with them) needs this block's weights done.
+      asm volatile("" : "+v"(lsum));
+    };
+    static_assert(BS / 32 * 2 == 8, "weight blocks below");
+    // The remaining copy pairs go out between the first weight blocks.
+    using std::integral_constant;
+    weights(integral_constant<int, 0>{});
+    copies(integral_constant<int, 2>{});
+    weights(integral_constant<int, 1>{});
+    copies(integral_constant<int, 3>{});
+    weights(integral_constant<int, 2>{});
+    copies(integral_constant<int, 4>{});
+    weights(integral_constant<int, 3>{});
+    copies(integral_constant<int, 5>{});
+    weights(integral_constant<int, 4>{});
+    copies(integral_constant<int, 6>{});
+    weights(integral_constant<int, 5>{});
+    copies(integral_constant<int, 7>{});
+    weights(integral_constant<int, 6>{});
+    weights(integral_constant<int, 7>{});
     if (pads_in_sum) {
       // Each pad key of this lane's half of the tile (bits 8g + {0..7,
-      // 16..23} of each validity word) got the bf16 weight of 2^(0 - m).
+      // 16..23} of each validity word) scored exactly 0 and so got the
+      // weight 2^(0 - m).
       uint32_t npad = 0;
 #pragma unroll
       for (int kb = 0; kb < BS / 32; ++kb)
         npad += __popc(~tile_bits[kt * 4 + kb] & (g ? 0xFF00FF00u : 0x00FF00FFu));
-      const float w_pad = float(__bf16(__builtin_amdgcn_exp2f(neg_m)));
-      lsum -= float(npad) * w_pad;
+      lsum -= float(npad) * __builtin_amdgcn_exp2f(neg_m);
     }
     l_run = lsum;
     // The wait stays after the softmax, which it would otherwise precede.
@@ -624,6 +663,10 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
   // group 0 combines them with its own and stores.
   float4* ob = reinterpret_cast<float4*>(lds);
   constexpr int kQuads = D / 32 * 4;
+  constexpr int kMergeBytes = C::kGroupWaves * kQuads * 64 * 16;
+  static_assert(kMergeBytes + 2 * C::kGroupWaves * 64 * 4 <= 4 * C::kTileBytes, "merge space");
+  float* const m_buf = reinterpret_cast<float*>(reinterpret_cast<char*>(lds) + kMergeBytes);
+  float* const l_buf = m_buf + C::kGroupWaves * 64;
   if (grp == 1) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)

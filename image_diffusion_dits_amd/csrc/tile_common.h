@@ -81,6 +81,31 @@ __device__ __forceinline__ void dma_tile(const char* base, int bytes, void* dst,
         u * kStride, 0, 0);
 }
 
+// The copies of dma_tile issued one at a time, so that a caller can spread
+// them between other instructions: a wave stalls at a tile copy while the
+// memory pipeline is still taking the previous ones, so a burst of copies
+// holds back the arithmetic queued behind it.
+template <int WAVES>
+struct TileCopy {
+  __amdgpu_buffer_rsrc_t rsrc;
+  char* dst;
+  uint32_t voff;
+  __device__ __forceinline__ TileCopy(const char* base, int bytes, void* lds, uint32_t v, int w)
+      : rsrc(__builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, bytes, kBufferWord3)),
+        voff(v) {
+    int woff = w * 1024;
+    asm volatile("" : "+s"(woff));
+    dst = static_cast<char*>(lds) + woff;
+  }
+  // Copy u: LDS [dst + u*WAVES*1024, +1024) from lane offset voff + u * the
+  // bytes one copy covers, as in dma_tile.
+  template <int U>
+  __device__ __forceinline__ void issue() const {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + U * WAVES * 1024), 16,
+                                             voff, U * WAVES * 64 * 16, 0, 0);
+  }
+};
+
 // As dma_tile, with copy u reading from lane offset voff + soff[u]: for
 // tiles whose LDS rows are a permutation of the global rows.
 template <int COPIES, int WAVES>

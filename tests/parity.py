@@ -9,12 +9,11 @@
   attention     bf16: max-abs <= 2e-2 and mean-abs <= 5e-3 over valid rows;
                 fp32: max-abs <= 1e-5.  The oracle row is computed with the
                 GPU's kept list, so a legal borderline swap cannot fail it.
-  log-sum-exp   bf16: |gpu - oracle| <= 4e-3 + 1e-6 |oracle|.  The kernel sums
-                the bf16-rounded weights (8-bit significand: relative error
-                at most 2^-8 each, so the sum is off by at most a factor
-                1 +- 2^-8 and its log by at most -ln(1 - 2^-8) = 3.92e-3);
-                the logits come from fp32 dot products of the same bf16
-                operands the oracle reads.
+  log-sum-exp   bf16: |gpu - oracle| <= 1e-4 + 1e-6 |oracle|.  The kernels
+                sum the fp32 weights (the bf16 rounding is applied only to
+                the PV operand), so the error is that of fp32 logits from
+                the same bf16 operands the oracle reads, a few ulp of the
+                dot products of 128 products, and of the fp32 sum.
                 fp32: <= 1e-5 + 1e-6 |oracle|.  Pad slots are -inf on both.
   dense mask    bit-exact against the kept rows it copies.
 """
@@ -27,7 +26,7 @@ from oracle import rainfusion_oracle as orc
 
 BORDER = 1e-4
 TOL = {"bf16": (2e-2, 5e-3), "f32": (1e-5, 1e-5)}
-LSE_TOL = {"bf16": 4e-3, "f32": 1e-5}
+LSE_TOL = {"bf16": 1e-4, "f32": 1e-5}
 
 
 def bits(t: torch.Tensor) -> np.ndarray:
