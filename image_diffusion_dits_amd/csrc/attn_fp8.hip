@@ -6,8 +6,12 @@
 //
 // The structure is the bf16 ping-pong kernel's (two groups of four waves per
 // 128-slot query tile, one phase apart: MFMA phase PV(i-1) then S(i), VALU
-// phase softmax(i) while the group's next K and V^T tiles are copied into
-// LDS).  What changes with 8-bit operands:
+// phase softmax(i)).  What changes with 8-bit operands:
+//   * tiles are 16 KB, so each group double-buffers K and V^T (128 KB of
+//     LDS) and starts the copies of K(i+1) and V^T(i) at the end of its MFMA
+//     phase of tile i, into the slots that phase did not read: the issue
+//     stalls of the copies fall in the wait at the barrier rather than in
+//     the softmax;
 //   * one MFMA reduces 64 features (or keys): 8 MFMAs for S and 8 for PV per
 //     tile and wave, each fed 32 bytes per lane (two 16-byte LDS reads);
 //   * P^T must reach the PV MFMA straight from the S^T accumulators.  Lane
@@ -62,12 +66,6 @@ __device__ inline f32x16 mma(const i32x8& a, const i32x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-__device__ inline i32x8 lds32(const uint8_t* row, int c0, int swz) {
-  const i32x4 lo = *reinterpret_cast<const i32x4*>(row + ((c0) ^ swz) * 16);
-  const i32x4 hi = *reinterpret_cast<const i32x4*>(row + ((c0 + 1) ^ swz) * 16);
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
 // Four e4m3 codes in one word.  The first conversion writes the low half and
 // keeps the high half of its `old` operand, which the second overwrites, so
 // `old` is any register (here a's): no zeroing move is needed.
@@ -85,8 +83,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
     int64_t Lt, int32_t BH, int32_t nb, int32_t n_tt, int32_t row_len_video, int64_t nnz,
     float scale_log2) {
   constexpr int kWaitVm0 = 0x0F70;     // s_waitcnt vmcnt(0)
-  // K and V^T tiles of group 0, then of group 1; reused for the merge.
-  __shared__ __align__(16) uint8_t lds[4 * kTileBytes];
+  // Two K and two V^T tiles per group (K(i) in K slot i % 2, V^T(i) in V
+  // slot i % 2); reused for the merge.
+  __shared__ __align__(16) uint8_t lds[8 * kTileBytes];
   __shared__ float m_buf[kGroupWaves * 64], l_buf[kGroupWaves * 64];
 
   const int32_t n_tiles = nb + n_tt;
@@ -98,8 +97,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
   const int qw = wave % kGroupWaves;
   const int lane = threadIdx.x % 64;
   const int li = lane % 32, g = lane / 32;
-  uint8_t* const ks = lds + (2 * grp) * kTileBytes;
-  uint8_t* const vs = lds + (2 * grp + 1) * kTileBytes;
+  uint8_t* const kslot = lds + (4 * grp) * kTileBytes;       // + (i % 2) * kTileBytes
+  uint8_t* const vslot = lds + (4 * grp + 2) * kTileBytes;
 
   const char* kh = reinterpret_cast<const char*>(k8 + bh * Lt * D);
   const char* vh = reinterpret_cast<const char*>(v8 + bh * int64_t(n_tiles) * D * BS);
@@ -143,15 +142,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
   const uint32_t koff = uint32_t(key0 * kRowBytes + (pc ^ swz_rows<kRowBytes>(xr)) * 16);
   const uint32_t ksoff[kCopies] = {0u, 16u * kRowBytes, 64u * kRowBytes, 80u * kRowBytes};
   const uint32_t voff = dma_offset<kRowBytes, kRowBytes, kGroupWaves>(qw, lane);
-  auto copy_k = [&](int32_t kt) {
+  auto copy_k = [&](int32_t kt, int par) {
     dma_tile_perm<kCopies, kGroupWaves>(kh + int64_t(max(kt, 0)) * kTileBytes, kTileBytes,
-                                        ks, koff, qw, ksoff);
+                                        kslot + par * kTileBytes, koff, qw, ksoff);
   };
-  auto copy_v = [&](int32_t kt) {
-    dma_tile<kCopies, kGroupWaves>(vh + int64_t(max(kt, 0)) * kTileBytes, kTileBytes, vs,
-                                   voff, qw);
+  auto copy_v = [&](int32_t kt, int par) {
+    dma_tile<kCopies, kGroupWaves>(vh + int64_t(max(kt, 0)) * kTileBytes, kTileBytes,
+                                   vslot + par * kTileBytes, voff, qw);
   };
   const int rswz = swz_rows<kRowBytes>(li);     // rows 32 kb + li and 32 db + li
+  // 32 bytes of row r at 16-byte chunks c0 and c0 + 1 (c0 = 4 step + 2g): the
+  // row offset and the two swizzled chunk offsets 16 ((2g + e) ^ swz) are
+  // passed through an empty asm at each phase, so the addresses of the
+  // current slots are derived there instead of held for both parities.
+  auto operand = [&](const uint8_t* rowp, int step, int x0, int x1) -> i32x8 {
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(rowp + ((64 * step) ^ x0));
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(rowp + ((64 * step) ^ x1));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
 
   constexpr int kAhead = 4;                     // MFMAs whose operands are read ahead
   auto pipeline_reads = [&]() {
@@ -182,41 +190,60 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
     return a;
   };
 
+  // Validity word w + g of tile kt (0 for a masked tile), read as two
+  // uniform scalar loads: a per-lane vector load would have to wait, in
+  // order, for every tile copy issued before it.
+  auto tile_word = [&](int32_t kt, int w) -> uint32_t {
+    if (kt < 0) return 0u;
+    const uint32_t w0 = tile_bits[kt * 4 + w], w1 = tile_bits[kt * 4 + w + 1];
+    return g ? w1 : w0;
+  };
+
   auto mfma_phase = [&](int32_t i) {
+    int lrow = li * kRowBytes, x0 = ((2 * g) ^ rswz) * 16, x1 = ((2 * g + 1) ^ rswz) * 16;
+    asm volatile("" : "+v"(lrow), "+v"(x0), "+v"(x1));
     if (i >= 1) {
       // O^T[db] += V^T[db rows, keys 64s .. +64] P^T(i-1), k-steps s = 0, 1.
+      const uint8_t* const vs = vslot + ((i - 1) & 1) * kTileBytes + lrow;
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
-          o[db] = mma(lds32(vs + (db * 32 + li) * kRowBytes, 4 * st + 2 * g, rswz), pb[st], o[db]);
+          o[db] = mma(operand(vs + db * 32 * kRowBytes, st, x0, x1), pb[st], o[db]);
       pipeline_reads();
       lsum = mma(row_sum_operand(0), pb[0], lsum);
       lsum = mma(row_sum_operand(1), pb[1], lsum);
     }
     __builtin_amdgcn_sched_barrier(0);
     if (i < n_grp) {
+      const uint8_t* const ks = kslot + (i & 1) * kTileBytes + lrow;
 #pragma unroll
       for (int kb = 0; kb < BS / 32; ++kb) {
         s[kb] = f32x16{};
 #pragma unroll
         for (int m = 0; m < 2; ++m)
-          s[kb] = mma(lds32(ks + (kb * 32 + li) * kRowBytes, 4 * m + 2 * g, rswz), qf[m], s[kb]);
+          s[kb] = mma(operand(ks + kb * 32 * kRowBytes, m, x0, x1), qf[m], s[kb]);
       }
       pipeline_reads();
+      // The copies of K(i+1) and V^T(i) go to the slots not read in this
+      // phase (they were last read in the group's previous MFMA phase), after
+      // this phase's LDS reads: their issue stalls fall in the wait at the
+      // barrier, and the group's VALU phase waits for them at its end.
+      __builtin_amdgcn_sched_barrier(0);
+      const int32_t kt = tile_of(i);
+      if (i + 1 < n_grp) copy_k(tile_of(i + 1), (i + 1) & 1);
+      copy_v(kt, i & 1);
     }
   };
 
   auto valu_phase = [&](int32_t i) {
     if (i < 0 || i >= n_grp) return;
     const int32_t kt = tile_of(i);
-    if (i + 1 < n_grp) copy_k(tile_of(i + 1));
-    copy_v(kt);
     const int32_t tcount = kt >= 0 ? tile_count[kt] : 0;
     const float c = c_q * (kt >= 0 ? ksc[kt] : 1.f);
     vw_full = tcount == BS;
 #pragma unroll
-    for (int st = 0; st < 2; ++st) vw[st] = kt >= 0 ? tile_bits[kt * 4 + 2 * st + g] : 0u;
+    for (int st = 0; st < 2; ++st) vw[st] = tile_word(kt, 2 * st);
     // Row max over the tile's raw dot products (the scale is positive).
     auto row_max = [&]() {
       float m = -INFINITY;
@@ -242,7 +269,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
 #pragma unroll
       for (int kb = 0; kb < BS / 32; ++kb) {
         const uint32_t pad =
-            ~((kt >= 0 ? tile_bits[kt * 4 + 2 * (kb / 2) + g] : 0u) >> (16 * (kb % 2)));
+            ~(tile_word(kt, 2 * (kb / 2)) >> (16 * (kb % 2)));
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const uint32_t m = uint32_t(int32_t(pad << (31 - r)) >> 31);
@@ -281,7 +308,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
     __builtin_amdgcn_s_waitcnt(kWaitVm0);   // the copies have landed
   };
 
-  if (n_grp > 0) copy_k(tile_of(0));
+  if (n_grp > 0) copy_k(tile_of(0), 0);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __builtin_amdgcn_s_barrier();
   if (grp == 0) {
