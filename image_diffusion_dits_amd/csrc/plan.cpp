@@ -362,4 +362,16 @@ rf_status rf_plan_sizes(const rf_plan* plan, rf_sizes* out) {
   return RF_OK;
 }
 
+rf_status rf_plan_info(const rf_plan* plan, int64_t* N, int64_t* Np, int32_t* nb,
+                       int32_t* bs, int32_t* n_sink, int32_t* n_text_tiles) {
+  if (plan == nullptr) return rf::fail(RF_ERR_INVALID_ARG, "rf_plan_info: null plan");
+  if (N) *N = plan->sz.N;
+  if (Np) *Np = plan->sz.Np;
+  if (nb) *nb = plan->sz.nb;
+  if (bs) *bs = plan->sz.bs;
+  if (n_sink) *n_sink = plan->sz.n_sink;
+  if (n_text_tiles) *n_text_tiles = plan->sz.n_text_tiles;
+  return RF_OK;
+}
+
 }  // extern "C"

@@ -59,6 +59,8 @@ _SIGNATURES = {
     "rf_keep_count": [_P(Layout), _c_i32, _P(Keep)],
     "rf_plan_create": [_P(Layout), _P(_vp)],
     "rf_plan_sizes": [_vp, _P(Sizes)],
+    "rf_plan_info": [_vp, _P(_c_i64), _P(_c_i64), _P(_c_i32), _P(_c_i32), _P(_c_i32),
+                     _P(_c_i32)],
     "rf_permute": [_vp, _vp, _vp, _c_i32, _c_i32, _c_i32, ctypes.c_int,
                    ctypes.c_int, _vp],
     "rf_permute_means": [_vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32,

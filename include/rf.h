@@ -181,6 +181,11 @@ typedef struct rf_plan rf_plan;   /* opaque: layout, sizes, device tables */
 rf_status rf_plan_create(const rf_layout* lay, rf_plan** out);
 void rf_plan_destroy(rf_plan* plan);
 rf_status rf_plan_sizes(const rf_plan* plan, rf_sizes* out);
+/* The same sizes one by one (each output pointer may be null): video tokens
+ * N, padded slots Np, video blocks nb, block size bs, sink blocks n_sink and
+ * text tiles n_text_tiles. */
+rf_status rf_plan_info(const rf_plan* plan, int64_t* N, int64_t* Np, int32_t* nb,
+                       int32_t* bs, int32_t* n_sink, int32_t* n_text_tiles);
 
 /* ---- hot path (asynchronous on `stream`) ------------------------------- */
 

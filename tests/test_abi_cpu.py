@@ -152,6 +152,7 @@ def test_gpu_entry_points_reject_bad_arguments_without_a_device():
     assert L.rf_arm_classify(buf, 0, buf, 4, 1, 0.9, buf, None, None) == rf.ERR_INVALID_ARG
     assert L.rf_arm_classify(None, 4, buf, 4, 1, 0.9, buf, None, None) == rf.ERR_INVALID_ARG
     assert L.rf_plan_sizes(None, None) == rf.ERR_INVALID_ARG
+    assert L.rf_plan_info(None, None, None, None, None, None, None) == rf.ERR_INVALID_ARG
     L.rf_plan_destroy(None)  # no-op
     assert L.rf_status_str(rf.ERR_HIP) == b"HIP runtime error"
 

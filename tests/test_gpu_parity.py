@@ -261,6 +261,15 @@ def test_out_of_range_kept_entries_are_skipped():
 def test_gpu_argument_errors():
     plan = rf.Plan(configs.TINY.layout)
     z = plan.sizes
+    # rf_plan_info gives the sizes of rf_plan_sizes one by one.
+    import ctypes
+    n, n_p = ctypes.c_int64(), ctypes.c_int64()
+    nb, bs, ns, nt = (ctypes.c_int32() for _ in range(4))
+    assert rf.lib().rf_plan_info(plan.handle, ctypes.byref(n), ctypes.byref(n_p),
+                                 ctypes.byref(nb), ctypes.byref(bs), ctypes.byref(ns),
+                                 ctypes.byref(nt)) == 0
+    assert (n.value, n_p.value, nb.value, bs.value, ns.value, nt.value) == \
+        (z["N"], z["Np"], z["nb"], z["bs"], z["n_sink"], z["n_text_tiles"])
     x = torch.zeros(1, 2, z["L"], 64, device="cuda")
     with pytest.raises(rf.RfError) as e:
         rf.permute(plan, x[..., :48].contiguous())       # d = 48
