@@ -46,24 +46,26 @@ __device__ inline int popc64(uint64_t m) { return __popcll(m); }
 //        kept set is {key >= t} and the search stops.
 //   keep key > tau, and of the keys == tau the lowest-indexed
 //   k_sel - #{key > tau}; the ascending compaction is a ballot prefix count.
-// The sink bits of lane l's blocks l + 64 m (bit m), the same for every row:
-// loaded once per wave, all loads in flight together.
+// The sink bits of lane l's blocks l + 64 m (bit m of a 64-bit mask, as
+// MMAX reaches 64), the same for every row: loaded once per wave, all loads
+// in flight together.
 template <int MMAX>
-__device__ __attribute__((always_inline)) uint32_t sink_bits(const uint8_t* __restrict__ is_sink,
+__device__ __attribute__((always_inline)) uint64_t sink_bits(const uint8_t* __restrict__ is_sink,
                                                              int nb, int lane) {
-  uint32_t sinkm = 0;
+  static_assert(MMAX <= 64, "one mask bit per register chunk");
+  uint64_t sinkm = 0;
 #pragma unroll
   for (int m = 0; m < MMAX; ++m) {
     const int j = lane + 64 * m;
     const uint32_t sk = is_sink[min(j, nb - 1)];
-    sinkm |= uint32_t(j < nb && sk != 0) << m;
+    sinkm |= uint64_t(j < nb && sk != 0) << m;
   }
   return sinkm;
 }
 
 template <int MMAX>
 __device__ __attribute__((always_inline)) void select_row(const float* __restrict__ row,
-                                                          uint32_t sinkm, int nb, int k_sel,
+                                                          uint64_t sinkm, int nb, int k_sel,
                                                           int k_eff, int n_tt,
                                                           int32_t* __restrict__ out, int lane) {
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -72,7 +74,7 @@ __device__ __attribute__((always_inline)) void select_row(const float* __restric
   for (int m = 0; m < MMAX; ++m) {
     const int j = lane + 64 * m;
     const uint32_t k = order_key(row[min(j, nb - 1)]);
-    key[m] = (j < nb && !((sinkm >> m) & 1u)) ? k : 0u;
+    key[m] = (j < nb && !((sinkm >> m) & 1ull)) ? k : 0u;
   }
   uint32_t tau = 0;
   if (k_sel > 0) {
@@ -97,7 +99,7 @@ __device__ __attribute__((always_inline)) void select_row(const float* __restric
 #pragma unroll
   for (int m = 0; m < MMAX; ++m) {
     const int j = lane + 64 * m;
-    const bool sink = (sinkm >> m) & 1u;
+    const bool sink = (sinkm >> m) & 1ull;
     const bool eq = k_sel > 0 && key[m] != 0 && key[m] == tau;
     bool keep = sink || (k_sel > 0 && key[m] > tau);
     const uint64_t eqm = __ballot(eq);
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void predict_mask_kernel(
 
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   const int k_sel = k_eff - n_sink;
-  const uint32_t sinkm = sink_bits<MMAX>(is_sink, nb, lane);
+  const uint64_t sinkm = sink_bits<MMAX>(is_sink, nb, lane);
   for (int r = wave; r < R; r += kWaves) {
     const int i = i0 + r;
     if (i >= nb) break;
@@ -230,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void predict_mask_mfma_kernel(
   }
   __syncthreads();
   const int k_sel = k_eff - n_sink;
-  const uint32_t sinkm = sink_bits<MMAX>(is_sink, nb, lane);
+  const uint64_t sinkm = sink_bits<MMAX>(is_sink, nb, lane);
   for (int r = wave; r < R; r += kWaves) {
     const int i = i0 + r;
     if (i >= nb) break;

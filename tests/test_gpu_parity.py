@@ -206,6 +206,18 @@ def test_sweep_workload(permute):
                    sample_tiles=12, seed=s)
 
 
+def test_more_than_1024_blocks_per_row():
+    """nb = 1088 (17 frames of 64x64 tokens, 1x8x8 windows) takes the mask
+    kernel for rows longer than the MFMA selection holds (nb > 1024)."""
+    lay = dict(T=17, H=64, W=64, wt=1, wh=8, ww=8, n_text=0, permute=1, sink=1)
+    z = rf.layout_sizes(lay)
+    assert z["nb"] == 1088
+    say(f"[edge] nb={z['nb']} bs=64 d=64 bf16 s=90 (all blocks: permutation, means, mask; "
+        f"attention: 24 sampled tiles)")
+    q, k, v = (_iid((1, 1, z["L"], 64), sd, torch.bfloat16) for sd in (21, 22, 23))
+    check_case(lay, q, k, v, 90, "bf16", full_heads=set(), sample_tiles=24, seed=5)
+
+
 def test_repeated_runs_are_bitwise_identical():
     cfg = configs.VIDEO720
     say("[determinism] three runs of the 720p case (8 heads)")
@@ -288,6 +300,13 @@ def test_gpu_argument_errors():
     st = L.rf_predict_mask(plan.handle, xp.data_ptr(), xp.data_ptr(), 1, 2, 64, 100,
                            kept.data_ptr(), None, None, None)
     assert st == rf.ERR_INVALID_ARG
+    # More than 4096 blocks per row is refused before any launch.
+    big = rf.Plan(dict(T=65, H=64, W=64, wt=1, wh=8, ww=8, n_text=0, permute=1, sink=1))
+    assert big.sizes["nb"] == 4160
+    st = L.rf_predict_mask(big.handle, xp.data_ptr(), xp.data_ptr(), 1, 1, 64, 50,
+                           kept.data_ptr(), None, None, None)
+    assert st == rf.ERR_UNSUPPORTED and b"4096" in L.rf_last_error()
+    big.close()
     # A misaligned LSE buffer is refused before any launch.
     st = L.rf_sparse_attn(plan.handle, xp.data_ptr(), xp.data_ptr(), xp.data_ptr(),
                           kept.data_ptr(), 50, xp.data_ptr(), xp.data_ptr() + 2, 1, 2,
