@@ -144,6 +144,8 @@ EDGE = [
                       sink=1), 1, 2, 128, torch.bfloat16, 0),
     ("max-s99", dict(T=3, H=13, W=21, wt=2, wh=8, ww=8, n_text=0, permute=1,
                      sink=0), 1, 2, 128, torch.bfloat16, 99),
+    ("frames-smaller-than-window", dict(T=4, H=3, W=5, wt=2, wh=8, ww=8, n_text=3,
+                                        permute=1, sink=1), 1, 2, 128, torch.bfloat16, 50),
 ]
 
 
@@ -206,15 +208,18 @@ def test_sweep_workload(permute):
                    sample_tiles=12, seed=s)
 
 
-def test_more_than_1024_blocks_per_row():
-    """nb = 1088 (17 frames of 64x64 tokens, 1x8x8 windows) takes the mask
-    kernel for rows longer than the MFMA selection holds (nb > 1024)."""
-    lay = dict(T=17, H=64, W=64, wt=1, wh=8, ww=8, n_text=0, permute=1, sink=1)
+@pytest.mark.parametrize("T,d", [(16, 128), (17, 64), (17, 128), (64, 64)],
+                         ids=["nb1024-d128", "nb1088-d64", "nb1088-d128", "nb4096-d64"])
+def test_mask_kernel_size_limits(T, d):
+    """Frames of 64x64 tokens in 1x8x8 windows give 64 blocks per frame:
+    nb = 1024 is the largest row of the MFMA selection kernel, 1088 and 4096
+    take the kernel for longer rows (4096 its largest)."""
+    lay = dict(T=T, H=64, W=64, wt=1, wh=8, ww=8, n_text=0, permute=1, sink=1)
     z = rf.layout_sizes(lay)
-    assert z["nb"] == 1088
-    say(f"[edge] nb={z['nb']} bs=64 d=64 bf16 s=90 (all blocks: permutation, means, mask; "
+    assert z["nb"] == 64 * T
+    say(f"[edge] nb={z['nb']} bs=64 d={d} bf16 s=90 (all blocks: permutation, means, mask; "
         f"attention: 24 sampled tiles)")
-    q, k, v = (_iid((1, 1, z["L"], 64), sd, torch.bfloat16) for sd in (21, 22, 23))
+    q, k, v = (_iid((1, 1, z["L"], d), sd, torch.bfloat16) for sd in (21, 22, 23))
     check_case(lay, q, k, v, 90, "bf16", full_heads=set(), sample_tiles=24, seed=5)
 
 
