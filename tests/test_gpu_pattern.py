@@ -110,6 +110,21 @@ def test_pattern_rows_and_attention_edge_layouts(case):
                          "bf16" if dt == torch.bfloat16 else "f32")
 
 
+def test_patterns_and_arm_above_1024_blocks():
+    """nb = 1088 (17 frames of 64x64 tokens, 1x8x8 windows): pattern rows of
+    all three kinds bit-exact, attention on them for sampled tiles, and ARM
+    recall on both samples."""
+    lay = dict(T=17, H=64, W=64, wt=1, wh=8, ww=8, n_text=0, permute=1, sink=1)
+    z = rf.layout_sizes(lay)
+    assert z["nb"] == 1088
+    say(f"[pattern edge] nb={z['nb']} bs=64 d=64 bf16 b=0.25 tau=2 (12 sampled tiles)")
+    q, k, v = (_iid((1, 3, z["L"], 64), s, torch.bfloat16) for s in (44, 45, 46))
+    band = orc.band_halfwidth(parity.olayout(lay), 0.25)
+    check_rows_attention(lay, q, k, v, np.array([PATTERNS], np.int32), band, 2, "bf16",
+                         sample_tiles=12)
+    check_arm(lay, q, k, band, 2, (16, 256))
+
+
 def test_pattern_attention_video720_workload():
     cfg = configs.VIDEO720
     say(f"[pattern workload] {cfg.name} (3 heads, 24 sampled tiles each)")

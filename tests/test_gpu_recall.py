@@ -101,6 +101,17 @@ def test_recall_tiny_and_image_workloads():
         check_recall(cfg.layout, q, k, cfg.sparsity[0])
 
 
+@pytest.mark.parametrize("T,d", [(17, 128), (64, 64)], ids=["nb1088-d128", "nb4096-d64"])
+def test_recall_at_large_block_counts(T, d):
+    """Rows longer than 1024 blocks, up to the mask kernel's 4096: recall of
+    the first, last and two random query tiles."""
+    lay = dict(T=T, H=64, W=64, wt=1, wh=8, ww=8, n_text=0, permute=1, sink=1)
+    z = rf.layout_sizes(lay)
+    say(f"[recall edge] nb={z['nb']} d={d} bf16 s=90")
+    q, k = (_iid((1, 1, z["L"], d), sd, torch.bfloat16) for sd in (31, 32))
+    check_recall(lay, q, k, 90)
+
+
 def test_recall_video720_workload():
     cfg = configs.VIDEO720
     say(f"[recall workload] {cfg.name} (4 heads)")
