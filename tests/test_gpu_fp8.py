@@ -276,6 +276,17 @@ def test_fp8_video720_workload():
     check_fp8_attention(cfg.layout, q, k, v, cfg.sparsity[0], sample_tiles=12)
 
 
+def test_fp8_above_1024_blocks():
+    """nb = 1088 (34 frames of 64x64 tokens, 2x8x8 windows): quantization
+    bit-exact on every tile, attention and LSE on 8 sampled tiles."""
+    lay = dict(T=34, H=64, W=64, wt=2, wh=8, ww=8, n_text=0, permute=1, sink=1)
+    z = rf.layout_sizes(lay)
+    assert z["nb"] == 1088
+    say(f"[fp8 edge] nb={z['nb']} (1 head, 8 sampled tiles)")
+    q, k, v = (_iid((1, 1, z["L"], 128), sd) for sd in (81, 82, 83))
+    check_fp8_attention(lay, q, k, v, 90, sample_tiles=8)
+
+
 def test_fp8_long_text_workload():
     cfg = configs.VIDEO_LONG
     z = rf.layout_sizes(cfg.layout)
