@@ -17,17 +17,27 @@ struct TileJob {
 };
 
 // Workgroup id -> (b*H + h, query tile).  Text query tiles of all heads come
-// first; video tiles are dealt so that ids landing on the same XCD (id mod 8)
-// cover a contiguous run of (head, tile).
+// first.  Video tiles, in (head, tile) order, are dealt in segments of
+// kXcds * kXcdWindow: XCD x (ids congruent to x mod 8) takes the x-th run of
+// kXcdWindow consecutive tiles of each segment.  The workgroups an XCD runs
+// at once then work on neighbouring tiles, which share many kept K/V tiles
+// through its L2, and all XCDs stay on the same head at a time, so the K/V
+// tiles they stream stay within the memory-side cache.  A final partial
+// segment is taken in id order.
+constexpr int kXcdWindow = 32;
+
 __device__ inline TileJob job_of(int32_t pid, int32_t BH, int32_t nb,
                                  int32_t n_tt) {
   const int32_t n_text_jobs = BH * n_tt;
   if (pid < n_text_jobs) return {pid / n_tt, nb + pid % n_tt};
   const int32_t p = pid - n_text_jobs;
-  const int32_t total = BH * nb;
-  const int32_t q = total / kXcds, r = total % kXcds;
-  const int32_t x = p % kXcds, idx = p / kXcds;
-  const int32_t logical = (x < r) ? x * (q + 1) + idx : r * (q + 1) + (x - r) * q + idx;
+  constexpr int32_t kSeg = kXcds * kXcdWindow;
+  const int32_t full = (BH * nb) / kSeg * kSeg;
+  int32_t logical = p;
+  if (p < full) {
+    const int32_t x = p % kXcds, idx = p / kXcds;
+    logical = (idx / kXcdWindow) * kSeg + x * kXcdWindow + idx % kXcdWindow;
+  }
   return {logical / nb, logical % nb};
 }
 
