@@ -20,6 +20,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -437,6 +438,8 @@ def main():
     stage_ms = {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / a.steps
                 for j, name in enumerate(stages)}
     ev_step_ms = sum(e[0].elapsed_time(e[n_ev - 1]) for e in evs) / a.steps
+    j_attn = stages.index("sparse_attn")
+    attn_median = statistics.median(e[j_attn].elapsed_time(e[j_attn + 1]) for e in evs)
 
     pairs = kc["nnz_per_head"] * B * H
     exec_flop = 4.0 * d * bs * bs * pairs
@@ -481,6 +484,7 @@ def main():
             "kept_tile_pairs": pairs, "sink_blocks": z["n_sink"],
         },
         "attn_ms": round(stage_ms["sparse_attn"], 4),
+        "attn_ms_median": round(attn_median, 4),
         "attn_exec_tflops": round(attn_tflops, 2),
         "attn_dense_equiv_tflops": round(dense_flop / attn_s / 1e12, 2),
         "mfma_util": round(attn_tflops / peak, 4),
