@@ -295,7 +295,8 @@ __global__ __launch_bounds__(kThreads) void permute_quant_tiles_t_kernel(
     const uint32_t* __restrict__ amax, const int32_t* __restrict__ slot_src, int64_t L,
     int32_t n_tiles) {
   constexpr int CPR = D / 8;            // 16-byte chunks per row
-  constexpr int ROW = D * 2 + 16;       // padded LDS row (bytes)
+  constexpr int ROW = D * 2;            // LDS row (bytes): chunk k of row s at k ^ ((s / 8) % CPR)
+  constexpr int SCN = BS / 8;           // 8-slot pieces per output row
   constexpr int NC = BS * CPR / kThreads;
   static_assert(BS * CPR % kThreads == 0, "chunk split");
   __shared__ __align__(16) uint8_t lds[BS * ROW];
@@ -314,19 +315,22 @@ __global__ __launch_bounds__(kThreads) void permute_quant_tiles_t_kernel(
 #pragma unroll
   for (int u = 0; u < NC; ++u) {
     const int c = threadIdx.x + u * kThreads;
-    *reinterpret_cast<uint4*>(lds + (c / CPR) * ROW + (c % CPR) * 16) = v[u];
+    const int s = c / CPR, k = c % CPR;
+    *reinterpret_cast<uint4*>(lds + s * ROW + (k ^ ((s / 8) % CPR)) * 16) = v[u];
   }
   __syncthreads();
-  // Sub-block (fc, sc): features fc*8 .. +8, slots sc*8 .. +8.
-  constexpr int NSUB = CPR * (BS / 8);
+  // Sub-block (fc, sc): features fc*8 .. +8, slots sc*8 .. +8.  Consecutive
+  // lanes take consecutive sc, so SCN lanes write one whole output row; the
+  // swizzle keeps the LDS stores and loads free of bank conflicts.
+  constexpr int NSUB = CPR * SCN;
   uint8_t* dst = x8 + (bh * n_tiles + tile) * int64_t(D) * BS;
   typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
   for (int b = threadIdx.x; b < NSUB; b += kThreads) {
-    const int fc = b % CPR, sc = b / CPR;
+    const int sc = b % SCN, fc = b / SCN;
     uint4 rows[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      rows[e] = *reinterpret_cast<const uint4*>(lds + (sc * 8 + e) * ROW + fc * 16);
+      rows[e] = *reinterpret_cast<const uint4*>(lds + (sc * 8 + e) * ROW + (fc ^ (sc % CPR)) * 16);
 #pragma unroll
     for (int f = 0; f < 8; ++f) {
       const int ex = pow2_exponent(__uint_as_float(amax[bh * D + fc * 8 + f]));
