@@ -236,7 +236,8 @@ __global__ __launch_bounds__(kThreads) void permute_quant_rows_kernel(
       f[2 * e + 1] = ldexpf(__uint_as_float(w[e] & 0xffff0000u), -ex);
     }
     const u32x2 out = {pack4(f[0], f[1], f[2], f[3]), pack4(f[4], f[5], f[6], f[7])};
-    *reinterpret_cast<u32x2*>(dst + int64_t(s) * D + k * VE) = out;
+    // Written once, read by the attention kernel later: no cache allocation.
+    __builtin_nontemporal_store(out, reinterpret_cast<u32x2*>(dst + int64_t(s) * D + k * VE));
   }
   if (xbar != nullptr && tile < nb && t < D) {
     float sum = 0.f;
@@ -339,7 +340,7 @@ __global__ __launch_bounds__(kThreads) void permute_quant_tiles_t_kernel(
       for (int e = 0; e < 8; ++e)
         y[e] = ldexpf(bf16_to_f32(reinterpret_cast<const uint16_t*>(&rows[e])[f]), -ex);
       const u32x2 out = {pack4(y[0], y[1], y[2], y[3]), pack4(y[4], y[5], y[6], y[7])};
-      *reinterpret_cast<u32x2*>(dst + int64_t(fc * 8 + f) * BS + sc * 8) = out;
+      __builtin_nontemporal_store(out, reinterpret_cast<u32x2*>(dst + int64_t(fc * 8 + f) * BS + sc * 8));
     }
   }
 }

@@ -141,7 +141,7 @@ __global__ __launch_bounds__(kThreads) void permute_tiles_t_kernel(
           t[e] = reinterpret_cast<const uint32_t*>(&rows[e])[f];
         out = *reinterpret_cast<const uint4*>(t);
       }
-      *reinterpret_cast<uint4*>(dst + (int64_t(fc * VE + f) * BS + sc * VE) * E) = out;
+      store_nt(dst + (int64_t(fc * VE + f) * BS + sc * VE) * E, out);
     }
   }
 }
