@@ -251,8 +251,9 @@ rf_status rf_predict_mask(const rf_plan* plan, const float* qbar,
  * query's log-sum-exp over its kept keys, ln sum_j exp(scale * q . k_j),
  * the natural-log softmax normaliser that merges this output with other
  * partial attentions; -inf at pad query slots and for a query with no
- * valid kept key.  With RF_BF16 the sum is that of the bf16 weights the
- * output uses.  d in {64, 128}. */
+ * valid kept key.  With RF_BF16 the sum is taken over the fp32 weights
+ * (the PV product uses them rounded to bf16), within about 1e-4 of the
+ * exact value.  d in {64, 128}. */
 rf_status rf_sparse_attn(const rf_plan* plan, const void* qp, const void* kp,
                          const void* vt, const int32_t* kept_idx,
                          int32_t sparsity_pct, void* op, float* lse_or_null,
