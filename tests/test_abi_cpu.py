@@ -201,3 +201,55 @@ def test_pattern_helpers_reject_bad_parameters():
     assert L.rf_arm_sample_count(ctypes.byref(lay), 1, 0, ctypes.byref(n)) == rf.ERR_INVALID_ARG
     small = np.empty(1, np.int32)
     assert L.rf_tile_rank(ctypes.byref(lay), small.ctypes.data, 1) == rf.ERR_BUFFER_TOO_SMALL
+
+
+class _HostPlan:
+    """The two members of rf.Plan that the row helpers read, from the host
+    functions alone (creating a real plan needs a device)."""
+
+    def __init__(self, lay):
+        self.layout = lay
+        self.sizes = rf.layout_sizes(lay)
+
+    def keep(self, sparsity_pct):
+        return rf.keep_count(self.layout, sparsity_pct)
+
+
+@pytest.mark.parametrize("lay,s", [
+    (dict(T=3, H=13, W=21, wt=2, wh=8, ww=8, n_text=77, permute=1, sink=1), 70),
+    (dict(T=3, H=7, W=11, wt=1, wh=8, ww=8, n_text=10, permute=0, sink=1), 60),
+    (dict(T=2, H=9, W=17, wt=2, wh=8, ww=8, n_text=0, permute=1, sink=0), 0),
+])
+def test_kept_rows_splits_the_flat_kept_list_into_the_oracle_rows(lay, s):
+    """The flat [B, H, nnz] kept list (video rows of equal length, then text
+    rows) splits back into the oracle's rows, head by head."""
+    import torch
+    olay = orc.Layout(**lay)
+    B, H, d = 2, 2, 64
+    rng = np.random.default_rng(7)
+    qbar = rng.standard_normal((B, H, orc.sizes(olay)["nb"], d))
+    kbar = rng.standard_normal((B, H, orc.sizes(olay)["nb"], d))
+    kept_o, _ = orc.predict_mask(qbar, kbar, olay, s)
+    flat = np.stack([np.stack([np.concatenate(kept_o[b][h]) for h in range(H)])
+                     for b in range(B)]).astype(np.int32)
+    plan = _HostPlan(lay)
+    assert flat.shape[2] == plan.keep(s)["nnz_per_head"]
+    rows = rf.kept_rows(plan, torch.from_numpy(flat), s)
+    for b in range(B):
+        for h in range(H):
+            assert len(rows[b][h]) == len(kept_o[b][h])
+            for got, want in zip(rows[b][h], kept_o[b][h]):
+                assert np.array_equal(got, want)
+
+
+def test_padded_rows_cut_each_row_at_its_first_negative_entry():
+    import torch
+    r = torch.tensor([[[[3, 5, 9, -1, -1],
+                        [0, 1, 2, 3, 4],
+                        [-1, 7, 8, -1, -1],
+                        [6, -1, 2, -1, 1]]]], dtype=torch.int32)
+    out = rf.padded_rows(r)
+    want = [[3, 5, 9], [0, 1, 2, 3, 4], [], [6]]
+    assert len(out) == 1 and len(out[0]) == 1
+    for got, w in zip(out[0][0], want):
+        assert got.tolist() == w
