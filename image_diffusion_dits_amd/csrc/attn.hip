@@ -876,7 +876,7 @@ extern "C" rf_status rf_sparse_attn(const rf_plan* plan, const void* qp,
                                     hipStream_t stream) {
   if (plan == nullptr) return rf::fail(RF_ERR_INVALID_ARG, "rf_sparse_attn: null plan");
   rf_keep kc;
-  rf_status st = rf_keep_count(&plan->lay, sparsity_pct, &kc);
+  rf_status st = rf_layout_keep(&plan->lay, sparsity_pct, &kc);
   if (st != RF_OK) return st;
   return sparse_attn(plan, qp, kp, vt, kept_idx, kc.row_len_video, kc.nnz_per_head,
                      op, lse_or_null, B, H, d, scale, dtype, stream, "rf_sparse_attn");

@@ -416,7 +416,7 @@ extern "C" rf_status rf_sparse_attn_fp8(const rf_plan* plan, const void* q8,
                                         hipStream_t stream) {
   if (plan == nullptr) return rf::fail(RF_ERR_INVALID_ARG, "rf_sparse_attn_fp8: null plan");
   rf_keep kc;
-  rf_status st = rf_keep_count(&plan->lay, sparsity_pct, &kc);
+  rf_status st = rf_layout_keep(&plan->lay, sparsity_pct, &kc);
   if (st != RF_OK) return st;
   return attn_fp8(plan, q8, q_scale, k8, k_scale, v8, v_scale, kept_idx, kc.row_len_video,
                   kc.nnz_per_head, op, lse_or_null, B, H, d, scale, stream,

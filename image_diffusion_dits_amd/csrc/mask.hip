@@ -276,9 +276,6 @@ void launch_mfma(const rf_plan* p, const float* qbar, const float* kbar,
                  hipStream_t st) {
   const int nb = p->sz.nb;
   const size_t lds = sizeof(float) * 16 * size_t(nb);
-  (void)hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&predict_mask_mfma_kernel<D, MMAX>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   dim3 grid((nb + 15) / 16, BH);
   hipLaunchKernelGGL((predict_mask_mfma_kernel<D, MMAX>), grid, dim3(kThreads), lds, st,
                      qbar, kbar, p->is_sink, kept, logits, nb, p->sz.n_sink,
@@ -303,9 +300,6 @@ void launch(const rf_plan* p, const float* qbar, const float* kbar,
             hipStream_t st) {
   const int nb = p->sz.nb;
   const size_t lds = sizeof(float) * (size_t(R) * D + size_t(R) * nb);
-  (void)hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&predict_mask_kernel<D, R, MMAX>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   dim3 grid((nb + R - 1) / R, BH);
   hipLaunchKernelGGL((predict_mask_kernel<D, R, MMAX>), grid, dim3(kThreads), lds, st,
                      qbar, kbar, p->is_sink, kept, logits, nb, p->sz.n_sink,
@@ -313,7 +307,39 @@ void launch(const rf_plan* p, const float* qbar, const float* kbar,
                      kc.nnz_per_head, 1.0f / sqrtf(float(D)));
 }
 
+template <int D, int MMAX>
+hipError_t allow_mfma_lds() {
+  // The largest row this instantiation serves: nb <= 64 MMAX (and <= 1024).
+  const int nb = 64 * MMAX < 1024 ? 64 * MMAX : 1024;
+  return hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&predict_mask_mfma_kernel<D, MMAX>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, int(sizeof(float) * 16 * nb));
+}
+
+template <int D, int R, int MMAX>
+hipError_t allow_lds() {
+  return hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&predict_mask_kernel<D, R, MMAX>),
+      hipFuncAttributeMaxDynamicSharedMemorySize,
+      int(sizeof(float) * (size_t(R) * D + size_t(R) * 4096)));
+}
+
 }  // namespace
+
+// Raises the dynamic-LDS limit of every mask kernel to the most it can ask
+// for, once per plan (at creation, on the plan's device) instead of on every
+// rf_predict_mask call.
+rf_status rf::prepare_mask_kernels() {
+  const hipError_t errs[] = {
+      allow_mfma_lds<128, 4>(), allow_mfma_lds<128, 8>(), allow_mfma_lds<128, 12>(),
+      allow_mfma_lds<128, 16>(), allow_mfma_lds<64, 4>(), allow_mfma_lds<64, 8>(),
+      allow_mfma_lds<64, 12>(), allow_mfma_lds<64, 16>(), allow_lds<128, 4, 64>(),
+      allow_lds<64, 4, 64>()};
+  for (hipError_t e : errs)
+    if (e != hipSuccess)
+      return rf::fail(RF_ERR_HIP, "mask kernel LDS limit: %s", hipGetErrorString(e));
+  return RF_OK;
+}
 
 extern "C" rf_status rf_predict_mask(const rf_plan* plan, const float* qbar,
                                      const float* kbar, int32_t B, int32_t H,
@@ -327,7 +353,7 @@ extern "C" rf_status rf_predict_mask(const rf_plan* plan, const float* qbar,
   if (logits_or_null != nullptr && !rf::aligned16(logits_or_null))
     return rf::fail(RF_ERR_INVALID_ARG, "rf_predict_mask: misaligned logits");
   rf_keep kc;
-  st = rf_keep_count(&plan->lay, sparsity_pct, &kc);
+  st = rf_layout_keep(&plan->lay, sparsity_pct, &kc);
   if (st != RF_OK) return st;
   const int nb = plan->sz.nb;
   // Dots of R rows x nb blocks must fit in LDS next to the R query rows.

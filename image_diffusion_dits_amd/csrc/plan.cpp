@@ -11,6 +11,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <vector>
 
 #include "rf_internal.h"
@@ -219,13 +220,13 @@ rf_status rf_layout_tables(const rf_layout* lay, int32_t* slot_src,
   return RF_OK;
 }
 
-rf_status rf_keep_count(const rf_layout* lay, int32_t sparsity_pct,
-                        rf_keep* out) {
+rf_status rf_layout_keep(const rf_layout* lay, int32_t sparsity_pct,
+                         rf_keep* out) {
   rf_sizes sz;
   rf_status st = compute_sizes(lay, &sz, nullptr);
   if (st != RF_OK) return st;
   if (out == nullptr)
-    return rf::fail(RF_ERR_INVALID_ARG, "rf_keep_count: null output");
+    return rf::fail(RF_ERR_INVALID_ARG, "rf_layout_keep: null output");
   if (sparsity_pct < 0 || sparsity_pct > 99)
     return rf::fail(RF_ERR_INVALID_ARG, "sparsity %d%% outside [0, 99]",
                     sparsity_pct);
@@ -238,6 +239,30 @@ rf_status rf_keep_count(const rf_layout* lay, int32_t sparsity_pct,
   out->row_len_text = sz.n_tiles;
   out->nnz_per_head = int64_t(sz.nb) * out->row_len_video +
                       int64_t(sz.n_text_tiles) * out->row_len_text;
+  return RF_OK;
+}
+
+rf_status rf_keep_count(const rf_plan* plan, int32_t sparsity_pct, int32_t* k_eff,
+                        int64_t* nnz_per_head) {
+  if (plan == nullptr) return rf::fail(RF_ERR_INVALID_ARG, "rf_keep_count: null plan");
+  rf_keep kc;
+  rf_status st = rf_layout_keep(&plan->lay, sparsity_pct, &kc);
+  if (st != RF_OK) return st;
+  if (k_eff) *k_eff = kc.k_eff;
+  if (nnz_per_head) *nnz_per_head = kc.nnz_per_head;
+  return RF_OK;
+}
+
+rf_status rf_band_tiles(const rf_layout* lay, double bandwidth, int32_t* band) {
+  rf_sizes sz;
+  rf_status st = compute_sizes(lay, &sz, nullptr);
+  if (st != RF_OK) return st;
+  if (band == nullptr) return rf::fail(RF_ERR_INVALID_ARG, "rf_band_tiles: null output");
+  if (!(bandwidth >= 0.0 && bandwidth <= 1.0))
+    return rf::fail(RF_ERR_INVALID_ARG, "bandwidth %g outside [0, 1]", bandwidth);
+  // Half-width of the band in video tiles, rounded to nearest (halves up):
+  // the band |i - j| <= w then covers 1 - (1 - b)^2 of the unit square.
+  *band = int32_t(std::floor(bandwidth * sz.nb + 0.5));
   return RF_OK;
 }
 
@@ -327,6 +352,8 @@ rf_status rf_plan_create(const rf_layout* lay, rf_plan** out) {
   if (e != hipSuccess)
     return rf::fail(RF_ERR_HIP, "rf_plan_create: no HIP device (%s)",
                     hipGetErrorString(e));
+  st = rf::prepare_mask_kernels();
+  if (st != RF_OK) return st;
   HostTables t;
   build_tables(*lay, sz, g, &t);
   rf_plan* p = new rf_plan();

@@ -254,7 +254,7 @@ extern "C" rf_status rf_attention_recall(const rf_plan* plan, const void* qp,
                                          float* recall_out, hipStream_t stream) {
   if (plan == nullptr) return rf::fail(RF_ERR_INVALID_ARG, "rf_attention_recall: null plan");
   rf_keep kc;
-  rf_status st = rf_keep_count(&plan->lay, sparsity_pct, &kc);
+  rf_status st = rf_layout_keep(&plan->lay, sparsity_pct, &kc);
   if (st != RF_OK) return st;
   return recall(plan, qp, kp, kept_idx, kc.row_len_video, kc.nnz_per_head, sample_tiles,
                 n_sample, B, H, d, scale, dtype, recall_out, stream, "rf_attention_recall");

@@ -27,6 +27,10 @@ rf_status fail(rf_status s, const char* fmt, ...);
 // Maps the last launch error, if any, to RF_ERR_HIP.
 rf_status check_launch(const char* what);
 
+// Sets the dynamic-LDS limits of the mask-prediction kernels on the current
+// device (called once by rf_plan_create).
+rf_status prepare_mask_kernels();
+
 inline bool aligned16(const void* p) {
   return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }

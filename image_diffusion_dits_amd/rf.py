@@ -56,7 +56,9 @@ _SIGNATURES = {
     "rf_layout_sizes": [_P(Layout), _P(Sizes)],
     "rf_layout_tables": [_P(Layout), _vp, _c_i64, _vp, _c_i64, _vp, _c_i64,
                          _vp, _c_i64],
-    "rf_keep_count": [_P(Layout), _c_i32, _P(Keep)],
+    "rf_layout_keep": [_P(Layout), _c_i32, _P(Keep)],
+    "rf_keep_count": [_vp, _c_i32, _P(_c_i32), _P(_c_i64)],
+    "rf_band_tiles": [_P(Layout), ctypes.c_double, _P(_c_i32)],
     "rf_plan_create": [_P(Layout), _P(_vp)],
     "rf_plan_sizes": [_vp, _P(Sizes)],
     "rf_plan_info": [_vp, _P(_c_i64), _P(_c_i64), _P(_c_i32), _P(_c_i32), _P(_c_i32),
@@ -166,10 +168,19 @@ def layout_tables(lay):
 
 
 def keep_count(lay, sparsity_pct):
+    """rf_layout_keep: the keep counts of a layout as a dict."""
     out = Keep()
-    _check(lib().rf_keep_count(ctypes.byref(_as_layout(lay)), int(sparsity_pct),
-                               ctypes.byref(out)), "rf_keep_count")
+    _check(lib().rf_layout_keep(ctypes.byref(_as_layout(lay)), int(sparsity_pct),
+                                ctypes.byref(out)), "rf_layout_keep")
     return out.as_dict()
+
+
+def band_tiles_of(lay, bandwidth):
+    """rf_band_tiles: band half-width in video tiles for a bandwidth fraction."""
+    w = _c_i32()
+    _check(lib().rf_band_tiles(ctypes.byref(_as_layout(lay)), float(bandwidth),
+                               ctypes.byref(w)), "rf_band_tiles")
+    return w.value
 
 
 def tile_rank(lay):
@@ -219,6 +230,13 @@ class Plan:
     def keep(self, sparsity_pct):
         return keep_count(self.layout, sparsity_pct)
 
+    def keep_count(self, sparsity_pct):
+        """rf_keep_count on the plan: (k_eff, nnz_per_head)."""
+        k, n = _c_i32(), _c_i64()
+        _check(lib().rf_keep_count(self._h, int(sparsity_pct), ctypes.byref(k),
+                                   ctypes.byref(n)), "rf_keep_count")
+        return k.value, n.value
+
     def close(self):
         if getattr(self, "_h", None):
             lib().rf_plan_destroy(self._h)
@@ -249,10 +267,71 @@ def _ptr(t):
     return _vp(t.data_ptr())
 
 
+def _on_device(t):
+    return t.is_cuda
+
+
 def _bhd(x):
-    if x.dim() != 4 or not x.is_contiguous() or not x.is_cuda:
+    if x.dim() != 4 or not x.is_contiguous() or not _on_device(x):
         raise ValueError("expected a contiguous CUDA tensor [B, H, tokens, d]")
     return x.shape[0], x.shape[1], x.shape[3]
+
+
+def _need(t, name, shape, dtypes, numel_only=False):
+    """Checks one tensor handed to the library against what the plan and the
+    call imply, before any launch: the kernels cannot check sizes and would
+    read or write past a short buffer.  shape: the expected shape (or, with
+    numel_only, the expected element count); dtypes: allowed dtypes."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: expected a tensor")
+    if not _on_device(t):
+        raise ValueError(f"{name}: expected a CUDA tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected one of {list(dtypes)}")
+    if numel_only:
+        if t.numel() != shape:
+            raise ValueError(f"{name}: {t.numel()} elements, expected {shape}")
+    elif tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+_FLOAT = (torch.bfloat16, torch.float32)
+_I32 = (torch.int32,)
+_F32 = (torch.float32,)
+_U8 = (torch.uint8,)
+
+
+def _rows_operands(plan, qp, kp, name="qp"):
+    """B, H, d of permuted RF_ROWS operands qp and kp, checked against the
+    plan (both [B, H, Lt, d] of one float dtype)."""
+    B, H, d = _bhd(qp)
+    Lt = plan.sizes["Lt"]
+    _need(qp, name, (B, H, Lt, d), _FLOAT)
+    if kp is not None:
+        _need(kp, "kp", (B, H, Lt, d), (qp.dtype,))
+    return B, H, d
+
+
+def _kept_operand(plan, kept, B, H, sparsity_pct):
+    nnz = plan.keep(sparsity_pct)["nnz_per_head"]
+    _need(kept, "kept", B * H * nnz, _I32, numel_only=True)
+
+
+def _rows_operand(plan, rows, B, H):
+    z = plan.sizes
+    if rows.dim() != 4:
+        raise ValueError("rows: expected [B, H, n_tiles, width]")
+    w = rows.shape[-1]
+    if not 1 <= w <= z["n_tiles"]:
+        raise ValueError(f"rows: width {w} outside [1, {z['n_tiles']}]")
+    _need(rows, "rows", (B, H, z["n_tiles"], w), _I32)
+
+
+def _vt_operand(plan, vt, B, H, d, dtypes):
+    z = plan.sizes
+    _need(vt, "vt", (B, H, z["n_tiles"], d, z["bs"]), dtypes)
 
 
 def permute(plan, x, order=ROWS, out=None):
@@ -260,12 +339,11 @@ def permute(plan, x, order=ROWS, out=None):
     z = plan.sizes
     if x.shape[2] != z["L"]:
         raise ValueError(f"x has {x.shape[2]} tokens, layout needs {z['L']}")
+    shape = (B, H, z["Lt"], d) if order == ROWS else (B, H, z["n_tiles"], d, z["bs"])
     if out is None:
-        if order == ROWS:
-            out = torch.empty(B, H, z["Lt"], d, dtype=x.dtype, device=x.device)
-        else:
-            out = torch.empty(B, H, z["n_tiles"], d, z["bs"], dtype=x.dtype,
-                              device=x.device)
+        out = torch.empty(shape, dtype=x.dtype, device=x.device)
+    _need(x, "x", (B, H, z["L"], d), _FLOAT)
+    _need(out, "out", shape, (x.dtype,))
     _check(lib().rf_permute(plan.handle, _ptr(x), _ptr(out), B, H, d,
                             _dtype_code(x), order, _stream()), "rf_permute")
     return out
@@ -281,6 +359,9 @@ def permute_means(plan, x, out=None, xbar=None):
         out = torch.empty(B, H, z["Lt"], d, dtype=x.dtype, device=x.device)
     if xbar is None:
         xbar = torch.empty(B, H, z["nb"], d, dtype=torch.float32, device=x.device)
+    _need(x, "x", (B, H, z["L"], d), _FLOAT)
+    _need(out, "out", (B, H, z["Lt"], d), (x.dtype,))
+    _need(xbar, "xbar", (B, H, z["nb"], d), _F32)
     _check(lib().rf_permute_means(plan.handle, _ptr(x), _ptr(out), _ptr(xbar), B,
                                   H, d, _dtype_code(x), _stream()),
            "rf_permute_means")
@@ -294,18 +375,22 @@ def unpermute(plan, xp, out=None):
         raise ValueError(f"xp has {xp.shape[2]} slots, layout needs {z['Lt']}")
     if out is None:
         out = torch.empty(B, H, z["L"], d, dtype=xp.dtype, device=xp.device)
+    _need(xp, "xp", (B, H, z["Lt"], d), _FLOAT)
+    _need(out, "out", (B, H, z["L"], d), (xp.dtype,))
     _check(lib().rf_unpermute(plan.handle, _ptr(xp), _ptr(out), B, H, d,
                               _dtype_code(xp), _stream()), "rf_unpermute")
     return out
 
 
 def block_means(plan, qp, kp, qbar=None, kbar=None):
-    B, H, d = _bhd(qp)
+    B, H, d = _rows_operands(plan, qp, kp)
     nb = plan.sizes["nb"]
     if qbar is None:
         qbar = torch.empty(B, H, nb, d, dtype=torch.float32, device=qp.device)
     if kbar is None:
         kbar = torch.empty_like(qbar)
+    _need(qbar, "qbar", (B, H, nb, d), _F32)
+    _need(kbar, "kbar", (B, H, nb, d), _F32)
     _check(lib().rf_block_means(plan.handle, _ptr(qp), _ptr(kp), _ptr(qbar),
                                 _ptr(kbar), B, H, d, _dtype_code(qp), _stream()),
            "rf_block_means")
@@ -318,10 +403,14 @@ def predict_mask(plan, qbar, kbar, sparsity_pct, kept=None, logits=False,
     logits [B, H, nb, nb], with dense=True also the uint8 tile mask
     [B, H, n_tiles, n_tiles], returned in that order after kept."""
     B, H, d = _bhd(qbar)
+    nb = plan.sizes["nb"]
+    _need(qbar, "qbar", (B, H, nb, d), _F32)
+    _need(kbar, "kbar", (B, H, nb, d), _F32)
     kc = plan.keep(sparsity_pct)
     if kept is None:
         kept = torch.empty(B, H, kc["nnz_per_head"], dtype=torch.int32,
                            device=qbar.device)
+    _kept_operand(plan, kept, B, H, sparsity_pct)
     lg = mask = None
     if logits:
         nb = plan.sizes["nb"]
@@ -348,11 +437,14 @@ def _lse_out(want, qp):
 def sparse_attn(plan, qp, kp, vt, kept, sparsity_pct, scale=None, out=None,
                 lse=False):
     """Op [B, H, Lt, d]; with lse=True also the fp32 log-sum-exp [B, H, Lt]."""
-    B, H, d = _bhd(qp)
+    B, H, d = _rows_operands(plan, qp, kp)
+    _vt_operand(plan, vt, B, H, d, (qp.dtype,))
+    _kept_operand(plan, kept, B, H, sparsity_pct)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(qp)
+    _need(out, "out", qp.shape, (qp.dtype,))
     lo = _lse_out(lse, qp)
     _check(lib().rf_sparse_attn(plan.handle, _ptr(qp), _ptr(kp), _ptr(vt),
                                 _ptr(kept), int(sparsity_pct), _ptr(out),
@@ -368,13 +460,16 @@ def attention_recall(plan, qp, kp, kept, sparsity_pct, sample_tiles, scale=None,
 
     sample_tiles: int32 tensor of query-tile ids on the device.  Returns fp32
     [B, H, n_sample, bs] (NaN at pad query slots)."""
-    B, H, d = _bhd(qp)
+    B, H, d = _rows_operands(plan, qp, kp)
+    _kept_operand(plan, kept, B, H, sparsity_pct)
+    n = sample_tiles.numel()
+    _need(sample_tiles, "sample_tiles", n, _I32, numel_only=True)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    n = sample_tiles.numel()
     if out is None:
         out = torch.empty((B, H, n, plan.sizes["bs"]), dtype=torch.float32,
                           device=qp.device)
+    _need(out, "out", (B, H, n, plan.sizes["bs"]), _F32)
     _check(lib().rf_attention_recall(plan.handle, _ptr(qp), _ptr(kp), _ptr(kept),
                                      int(sparsity_pct), _ptr(sample_tiles), n, B, H,
                                      d, float(scale), _dtype_code(qp), _ptr(out),
@@ -385,11 +480,14 @@ def attention_recall(plan, qp, kp, kept, sparsity_pct, sample_tiles, scale=None,
 
 def sparse_attn_rows(plan, qp, kp, vt, rows, scale=None, out=None, lse=False):
     """rf_sparse_attn on padded kept rows: rows is int32 [B, H, n_tiles, width]."""
-    B, H, d = _bhd(qp)
+    B, H, d = _rows_operands(plan, qp, kp)
+    _vt_operand(plan, vt, B, H, d, (qp.dtype,))
+    _rows_operand(plan, rows, B, H)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(qp)
+    _need(out, "out", qp.shape, (qp.dtype,))
     lo = _lse_out(lse, qp)
     _check(lib().rf_sparse_attn_rows(plan.handle, _ptr(qp), _ptr(kp), _ptr(vt),
                                      _ptr(rows), rows.shape[-1], _ptr(out),
@@ -401,13 +499,16 @@ def sparse_attn_rows(plan, qp, kp, vt, rows, scale=None, out=None, lse=False):
 
 def attention_recall_rows(plan, qp, kp, rows, sample_tiles, scale=None, out=None):
     """rf_attention_recall on padded kept rows [B, H, n_tiles, width]."""
-    B, H, d = _bhd(qp)
+    B, H, d = _rows_operands(plan, qp, kp)
+    _rows_operand(plan, rows, B, H)
+    n = sample_tiles.numel()
+    _need(sample_tiles, "sample_tiles", n, _I32, numel_only=True)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    n = sample_tiles.numel()
     if out is None:
         out = torch.empty((B, H, n, plan.sizes["bs"]), dtype=torch.float32,
                           device=qp.device)
+    _need(out, "out", (B, H, n, plan.sizes["bs"]), _F32)
     _check(lib().rf_attention_recall_rows(plan.handle, _ptr(qp), _ptr(kp), _ptr(rows),
                                           rows.shape[-1], _ptr(sample_tiles), n, B,
                                           H, d, float(scale), _dtype_code(qp),
@@ -417,20 +518,24 @@ def attention_recall_rows(plan, qp, kp, rows, sample_tiles, scale=None, out=None
 
 
 def band_tiles(plan, bandwidth):
-    """Band half-width in tiles for a bandwidth fraction: floor(b nb + 1/2)."""
-    return int(math.floor(bandwidth * plan.sizes["nb"] + 0.5))
+    """Band half-width in tiles of the plan's layout (rf_band_tiles)."""
+    return band_tiles_of(plan.layout, bandwidth)
 
 
 def pattern_mask(plan, head_pattern, band, tau=2, width=None, out=None):
     """Padded kept rows [B, H, n_tiles, width] of the v1 head patterns.
     head_pattern: int32 [B, H] on the device."""
+    if head_pattern.dim() != 2:
+        raise ValueError("head_pattern: expected [B, H]")
     B, H = head_pattern.shape
+    _need(head_pattern, "head_pattern", (B, H), _I32)
     if width is None:
         width = pattern_row_width(plan.layout, band, tau)
     if out is None:
         out = torch.empty((B, H, plan.sizes["n_tiles"], width), dtype=torch.int32,
                           device=head_pattern.device)
-    _check(lib().rf_pattern_mask(plan.handle, _ptr(head_pattern.contiguous()), B, H,
+    _rows_operand(plan, out, B, H)
+    _check(lib().rf_pattern_mask(plan.handle, _ptr(head_pattern), B, H,
                                  int(band), int(tau), _ptr(out), out.shape[-1],
                                  _stream()), "rf_pattern_mask")
     return out
@@ -440,12 +545,13 @@ def arm_recall(plan, qp, kp, local, stride, pattern, band, tau=2, scale=None,
                out=None):
     """Per sampled query, the share of its mass over the sampled keys that
     the pattern keeps: fp32 [B, H, n]."""
-    B, H, d = _bhd(qp)
+    B, H, d = _rows_operands(plan, qp, kp)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     n = arm_sample_count(plan.layout, local, stride)
     if out is None:
         out = torch.empty((B, H, n), dtype=torch.float32, device=qp.device)
+    _need(out, "out", (B, H, n), _F32)
     _check(lib().rf_arm_recall(plan.handle, _ptr(qp), _ptr(kp), int(bool(local)),
                                int(stride), int(pattern), int(band), int(tau), B, H,
                                d, float(scale), _dtype_code(qp), _ptr(out),
@@ -456,12 +562,18 @@ def arm_recall(plan, qp, kp, local, stride, pattern, band, tau=2, scale=None,
 def arm_classify(local_recall, global_recall, alpha=0.9, pattern=None, mean=None):
     """Head patterns (int32 [B, H]) and mean recalls (fp32 [B, H, 2]) from
     the two recall samples [B, H, n_local] and [B, H, n_global]."""
+    if local_recall.dim() != 3 or global_recall.dim() != 3:
+        raise ValueError("recalls: expected [B, H, n]")
     B, H, nl = local_recall.shape
     ng = global_recall.shape[-1]
+    _need(local_recall, "local_recall", (B, H, nl), _F32)
+    _need(global_recall, "global_recall", (B, H, ng), _F32)
     if pattern is None:
         pattern = torch.empty((B, H), dtype=torch.int32, device=local_recall.device)
     if mean is None:
         mean = torch.empty((B, H, 2), dtype=torch.float32, device=local_recall.device)
+    _need(pattern, "pattern", (B, H), _I32)
+    _need(mean, "mean", (B, H, 2), _F32)
     _check(lib().rf_arm_classify(_ptr(local_recall), nl, _ptr(global_recall), ng,
                                  B * H, float(alpha), _ptr(pattern), _ptr(mean),
                                  _stream()), "rf_arm_classify")
@@ -482,13 +594,21 @@ def quantize_fp8(plan, xp, order=ROWS, out=None, scale=None):
     """e4m3 codes (uint8, same shape as xp) and power-of-two scales of a
     permuted bf16 tensor: per tile for RF_ROWS ([B, H, n_tiles]), per
     feature for RF_TILES_T ([B, H, d])."""
+    z = plan.sizes
+    if xp.dim() != (4 if order == ROWS else 5):
+        raise ValueError("xp: expected [B, H, Lt, d] (RF_ROWS) or "
+                         "[B, H, n_tiles, d, bs] (RF_TILES_T)")
     B, H = xp.shape[:2]
     d = xp.shape[3]
+    shape = (B, H, z["Lt"], d) if order == ROWS else (B, H, z["n_tiles"], d, z["bs"])
+    _need(xp, "xp", shape, _FLOAT)
     if out is None:
         out = torch.empty(xp.shape, dtype=torch.uint8, device=xp.device)
+    n = z["n_tiles"] if order == ROWS else d
     if scale is None:
-        n = plan.sizes["n_tiles"] if order == ROWS else d
         scale = torch.empty((B, H, n), dtype=torch.float32, device=xp.device)
+    _need(out, "out", shape, _U8)
+    _need(scale, "scale", (B, H, n), _F32)
     _check(lib().rf_quantize_fp8(plan.handle, _ptr(xp), order, _ptr(out), _ptr(scale),
                                  B, H, d, _dtype_code(xp), _stream()), "rf_quantize_fp8")
     return out, scale
@@ -502,29 +622,51 @@ def permute_fp8(plan, x, order=ROWS, means=False, out=None, scale=None, xbar=Non
     z = plan.sizes
     if x.shape[2] != z["L"]:
         raise ValueError(f"x has {x.shape[2]} tokens, layout needs {z['L']}")
+    shape = (B, H, z["Lt"], d) if order == ROWS else (B, H, z["n_tiles"], d, z["bs"])
     if out is None:
-        shape = (B, H, z["Lt"], d) if order == ROWS else (B, H, z["n_tiles"], d, z["bs"])
         out = torch.empty(shape, dtype=torch.uint8, device=x.device)
+    n = z["n_tiles"] if order == ROWS else d
     if scale is None:
-        n = z["n_tiles"] if order == ROWS else d
         scale = torch.empty((B, H, n), dtype=torch.float32, device=x.device)
     if means and xbar is None:
         xbar = torch.empty((B, H, z["nb"], d), dtype=torch.float32, device=x.device)
+    _need(x, "x", (B, H, z["L"], d), _FLOAT)
+    _need(out, "out", shape, _U8)
+    _need(scale, "scale", (B, H, n), _F32)
+    if means:
+        _need(xbar, "xbar", (B, H, z["nb"], d), _F32)
     _check(lib().rf_permute_fp8(plan.handle, _ptr(x), order, _ptr(out), _ptr(scale),
                                 _ptr(xbar) if means else None, B, H, d, _dtype_code(x),
                                 _stream()), "rf_permute_fp8")
     return (out, scale, xbar) if means else (out, scale)
 
 
+def _fp8_operands(plan, q8, qs, k8, ks, v8, vs):
+    """B, H, d of the e4m3 attention operands, checked against the plan."""
+    if q8.dim() != 4:
+        raise ValueError("q8: expected [B, H, Lt, d]")
+    z = plan.sizes
+    B, H, _, d = q8.shape
+    _need(q8, "q8", (B, H, z["Lt"], d), _U8)
+    _need(k8, "k8", (B, H, z["Lt"], d), _U8)
+    _need(qs, "q_scale", (B, H, z["n_tiles"]), _F32)
+    _need(ks, "k_scale", (B, H, z["n_tiles"]), _F32)
+    _need(v8, "v8", (B, H, z["n_tiles"], d, z["bs"]), _U8)
+    _need(vs, "v_scale", (B, H, d), _F32)
+    return B, H, d
+
+
 def sparse_attn_fp8(plan, q8, qs, k8, ks, v8, vs, kept, sparsity_pct, scale=None,
                     out=None, lse=False):
     """Block-sparse attention on e4m3 operands; bf16 output [B, H, Lt, d]
     (and with lse=True the fp32 log-sum-exp [B, H, Lt])."""
-    B, H, _, d = q8.shape
+    B, H, d = _fp8_operands(plan, q8, qs, k8, ks, v8, vs)
+    _kept_operand(plan, kept, B, H, sparsity_pct)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
+    _need(out, "out", q8.shape, (torch.bfloat16,))
     lo = _lse_out(lse, q8)
     _check(lib().rf_sparse_attn_fp8(plan.handle, _ptr(q8), _ptr(qs), _ptr(k8), _ptr(ks),
                                     _ptr(v8), _ptr(vs), _ptr(kept), int(sparsity_pct),
@@ -536,11 +678,13 @@ def sparse_attn_fp8(plan, q8, qs, k8, ks, v8, vs, kept, sparsity_pct, scale=None
 
 def sparse_attn_fp8_rows(plan, q8, qs, k8, ks, v8, vs, rows, scale=None, out=None,
                          lse=False):
-    B, H, _, d = q8.shape
+    B, H, d = _fp8_operands(plan, q8, qs, k8, ks, v8, vs)
+    _rows_operand(plan, rows, B, H)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
+    _need(out, "out", q8.shape, (torch.bfloat16,))
     lo = _lse_out(lse, q8)
     _check(lib().rf_sparse_attn_fp8_rows(plan.handle, _ptr(q8), _ptr(qs), _ptr(k8),
                                          _ptr(ks), _ptr(v8), _ptr(vs), _ptr(rows),

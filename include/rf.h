@@ -147,9 +147,17 @@ rf_status rf_layout_tables(const rf_layout* lay, int32_t* slot_src,
                            int64_t cap_is_sink);
 
 /* Keep counts for sparsity_pct in [0, 99] [RF2 Abstract: 80% sparsity;
- * Figure 2: 60% for image editing]. */
-rf_status rf_keep_count(const rf_layout* lay, int32_t sparsity_pct,
-                        rf_keep* out);
+ * Figure 2: 60% for image editing], from a layout.  RF_ERR_INVALID_ARG for
+ * a null output or a sparsity outside [0, 99]. */
+rf_status rf_layout_keep(const rf_layout* lay, int32_t sparsity_pct,
+                         rf_keep* out);
+
+/* Band half-width, in video tiles, of the v1 band patterns for a bandwidth
+ * fraction b in [0, 1] [RF1 review, free parameters: bandwidth 1/4 giving a
+ * 9/16 cut]: *band = floor(b*nb + 1/2), so that the band |i - j| <= band
+ * keeps 1 - (1 - b)^2 of the video tile pairs (7/16 at b = 1/4).
+ * RF_ERR_INVALID_ARG for b outside [0, 1] or a null output. */
+rf_status rf_band_tiles(const rf_layout* lay, double bandwidth, int32_t* band);
 
 /* r(i) of RF_TEMPORAL for every video tile, into a host buffer of at least
  * nb elements (a permutation of 0..nb-1). */
@@ -186,6 +194,16 @@ rf_status rf_plan_sizes(const rf_plan* plan, rf_sizes* out);
  * text tiles n_text_tiles. */
 rf_status rf_plan_info(const rf_plan* plan, int64_t* N, int64_t* Np, int32_t* nb,
                        int32_t* bs, int32_t* n_sink, int32_t* n_text_tiles);
+
+/* Keep counts of the plan's layout for sparsity_pct in [0, 99] (the rule of
+ * rf_layout_keep [RF2 Abstract insights (1), (3)]): *k_eff = video blocks
+ * kept per video query row, *nnz_per_head = int32 entries of one head's
+ * kept list, the size of the kept_idx buffer per (b, h) that
+ * rf_predict_mask writes and rf_sparse_attn reads.  Either output may be
+ * null.  RF_ERR_INVALID_ARG for a null plan or a sparsity outside [0, 99].
+ * Host only: reads no device memory. */
+rf_status rf_keep_count(const rf_plan* plan, int32_t sparsity_pct, int32_t* k_eff,
+                        int64_t* nnz_per_head);
 
 /* ---- hot path (asynchronous on `stream`) ------------------------------- */
 
@@ -244,6 +262,13 @@ rf_status rf_predict_mask(const rf_plan* plan, const float* qbar,
  * tile i: o = sum_j softmax_j(scale * q . k_j) v_j over the valid slots of
  * the tiles listed in row i of kept_idx; pad query rows are written as 0.
  * qp, kp, op: [B][H][Lt][d] RF_ROWS; vt: [B][H][n_tiles][d][bs] RF_TILES_T.
+ * Precondition: the pad slots of kp (its rows at pad slots) and of vt (its
+ * columns at pad slots) hold zeros, as rf_permute writes them.  The
+ * 128-slot kernels rely on it: a pad key then scores exactly 0 and adds
+ * nothing to o, so they leave pad keys unmasked when every query's tile
+ * maximum is positive and take the pads' weights out of the row sum; with
+ * other pad values the result is unspecified (finite pad values give a
+ * finite result).  Pad query rows of qp are not read.
  * kept_idx as produced by rf_predict_mask for the same sparsity_pct; every
  * entry must lie in [0, n_tiles).  RF_BF16: bf16 operands, fp32
  * accumulation and softmax, bf16 output; RF_F32: fp32 throughout.
@@ -288,7 +313,8 @@ rf_status rf_attention_recall(const rf_plan* plan, const void* qp,
  * followed by -1 up to row_width (the length of a row is the position of
  * its first negative entry; an empty row gives output 0).  Entries outside
  * [0, n_tiles) before the first -1 are skipped.  1 <= row_width <= n_tiles.
- * Otherwise identical to rf_sparse_attn / rf_attention_recall. */
+ * Otherwise identical to rf_sparse_attn / rf_attention_recall (including
+ * the zero-pad precondition on kp and vt). */
 rf_status rf_sparse_attn_rows(const rf_plan* plan, const void* qp,
                               const void* kp, const void* vt,
                               const int32_t* kept_rows, int32_t row_width,
@@ -377,7 +403,9 @@ rf_status rf_permute_fp8(const rf_plan* plan, const void* x, rf_order order,
 /* Block-sparse attention on e4m3 operands: q8, k8 [B][H][Lt][d] (RF_ROWS)
  * with per-tile scales q_scale, k_scale [B][H][n_tiles]; v8
  * [B][H][n_tiles][d][bs] (RF_TILES_T) with per-feature scales v_scale
- * [B][H][d] (16-byte aligned), all from rf_quantize_fp8.  For each valid
+ * [B][H][d] (16-byte aligned), all from rf_quantize_fp8.  The pad slots of
+ * k8 and v8 must hold zero codes, as rf_quantize_fp8 and rf_permute_fp8
+ * write them (the precondition of rf_sparse_attn).  For each valid
  * query slot: o = sum_j w_j (v8_j * v_scale) / sum_j w_j over the valid
  * slots of the kept tiles, w_j = the e4m3 rounding of 16 exp(x_j - m) for
  * the logit x_j = scale * (q8 . k8_j) * q_scale * k_scale and a running

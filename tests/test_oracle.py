@@ -816,6 +816,129 @@ def test_fp8_attention_is_exact_on_representable_inputs():
     np.testing.assert_array_equal(a, b)
 
 
+def _closed_form_exponent(amax):
+    """e = ceil(log2(amax / 448)) for amax > 0, checked against the defining
+    inequality 224 < amax / 2^e <= 448; 0 for amax = 0."""
+    if amax == 0:
+        return 0
+    m, ex = math.frexp(amax / 448.0)       # amax / 448 = m 2^ex, m in [1/2, 1)
+    e = ex if m > 0.5 else ex - 1          # exact powers of two need no round-up
+    assert 224.0 < amax / 2.0 ** e <= 448.0
+    return e
+
+
+def _torch_e4m3(x):
+    """Round to e4m3 with torch's CPU float8_e4m3fn conversion (a library
+    routine), back to fp64."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, np.float64)).to(
+        torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _features_of_mixed_range(seed, lay, d=8):
+    """A permuted tensor whose features span very different ranges (feature f
+    scaled by 4^(f - 3), so its maximum ranges over some 2^12), sigma ~ 3,
+    with a few values in the subnormal range of their feature's scale."""
+    z = orc.sizes(lay)
+    r = _rng(seed)
+    x = r.standard_normal((1, 2, z["L"], d)) * 3.0 * 4.0 ** (np.arange(d) - 3)
+    x[0, 0, :5, 2] *= 2.0 ** -14                       # deep in the subnormal steps
+    return orc.permute(x, lay)
+
+
+def test_quantize_channels_values_equal_library_e4m3_per_feature():
+    """RF2 TL;DR (quantization as future work), reading R12, V operand: one
+    power-of-two scale per (b, h, feature) over all slots.  Independent
+    construction: the scale from the closed form of the exponent, torch's
+    float8_e4m3fn conversion of x 2^-e, times 2^e.  Every dequantized value
+    and exponent must match, and the error must stay within half an e4m3 step
+    (2^-4 relative for normal codes, 2^(e-10) in the subnormal range)."""
+    lay = orc.Layout(3, 5, 7, 2, 2, 4, n_text=9)
+    xp = _features_of_mixed_range(103, lay)
+    got, ex = orc.quantize_channels(xp)
+    B, H, Lp, d = xp.shape
+    want = np.empty_like(xp)
+    for b in range(B):
+        for h in range(H):
+            for f in range(d):
+                e = _closed_form_exponent(np.abs(xp[b, h, :, f]).max())
+                assert ex[b, h, f] == e, (b, h, f)
+                want[b, h, :, f] = _torch_e4m3(xp[b, h, :, f] * 2.0 ** -e) * 2.0 ** e
+                err = np.abs(got[b, h, :, f] - xp[b, h, :, f])
+                tol = np.maximum(np.abs(xp[b, h, :, f]) * 2.0 ** -4, 2.0 ** (e - 10))
+                assert np.all(err <= tol), (b, h, f, err.max())
+    np.testing.assert_array_equal(got, want)
+    # pad slots (zero) stay zero
+    assert np.all(got[:, :, ~orc.slot_valid(lay)] == 0)
+
+
+def test_quantize_channels_pin_rejects_wrong_direction_and_grouping():
+    """The data of the per-feature pin separates the two plausible mistakes:
+    scaling the wrong way (e4m3(x 2^e) 2^-e) and one scale per tile (as for
+    Q and K) instead of per feature both give values that differ from the
+    per-feature construction, so either mistake fails the pin above."""
+    lay = orc.Layout(3, 5, 7, 2, 2, 4, n_text=9)
+    z = orc.sizes(lay)
+    xp = _features_of_mixed_range(103, lay)
+    good, ex = orc.quantize_channels(xp)
+    # wrong direction; values beyond the e4m3 range saturate to keep it finite
+    flipped = np.empty_like(xp)
+    for f in range(xp.shape[-1]):
+        s = 2.0 ** ex[:, :, None, f]
+        flipped[..., f] = np.clip(_torch_e4m3(np.clip(xp[..., f] * s, -448, 448)), -448, 448) / s
+    assert not np.array_equal(flipped, good)
+    # per-tile grouping
+    tiled = np.empty_like(xp)
+    bs = z["bs"]
+    for t in range(z["n_tiles"]):
+        rows = slice(t * bs, min((t + 1) * bs, z["Lp"]))
+        for b in range(xp.shape[0]):
+            for h in range(xp.shape[1]):
+                e = _closed_form_exponent(np.abs(xp[b, h, rows]).max())
+                tiled[b, h, rows] = _torch_e4m3(xp[b, h, rows] * 2.0 ** -e) * 2.0 ** e
+    assert not np.array_equal(tiled, good)
+    # and per-tile scales break the per-feature half-step bound on the
+    # features of small range, whose values fall into coarse subnormal steps
+    bound = np.maximum(np.abs(xp) * 2.0 ** -4, 2.0 ** (ex[:, :, None, :] - 10))
+    assert np.any(np.abs(tiled - xp) > bound)
+    assert np.all(np.abs(good - xp) <= bound)
+
+
+def test_fp8_attention_uses_per_tile_qk_and_per_feature_v():
+    """sparse_attention_fp8 equals the plain attention on operands built
+    independently: Q and K with one closed-form scale per (b, h, tile) and V
+    with one per (b, h, feature), each rounded by torch's e4m3 conversion."""
+    lay = orc.Layout(3, 5, 7, 2, 2, 4, n_text=9, sink=1)
+    z = orc.sizes(lay)
+    r = _rng(107)
+    qp, kp = (orc.permute(r.standard_normal((1, 1, z["L"], 8)) * 3, lay) for _ in range(2))
+    vp = _features_of_mixed_range(109, lay)[:, :1]
+    kept, _ = orc.predict_mask(orc.block_means(qp, lay), orc.block_means(kp, lay), lay, 40)
+
+    def per_tile(x):
+        out = np.empty_like(x)
+        bs = z["bs"]
+        for t in range(z["n_tiles"]):
+            rows = slice(t * bs, min((t + 1) * bs, z["Lp"]))
+            e = _closed_form_exponent(np.abs(x[0, 0, rows]).max())
+            out[0, 0, rows] = _torch_e4m3(x[0, 0, rows] * 2.0 ** -e) * 2.0 ** e
+        return out
+
+    def per_feature(x):
+        out = np.empty_like(x)
+        for f in range(x.shape[-1]):
+            e = _closed_form_exponent(np.abs(x[0, 0, :, f]).max())
+            out[0, 0, :, f] = _torch_e4m3(x[0, 0, :, f] * 2.0 ** -e) * 2.0 ** e
+        return out
+
+    want = orc.sparse_attention(per_tile(qp), per_tile(kp), per_feature(vp), kept, lay)
+    got = orc.sparse_attention_fp8(qp, kp, vp, kept, lay)
+    np.testing.assert_array_equal(got, want)
+    # per-tile V would change the result on these features
+    alt = orc.sparse_attention(per_tile(qp), per_tile(kp), per_tile(vp), kept, lay)
+    assert not np.allclose(alt, want, atol=1e-6, equal_nan=True)
+
+
 # ---------------------------------------------------------- LSE and dense mask
 
 @pytest.mark.parametrize("n_text,permute", [(0, 1), (5, 1), (3, 0)])
