@@ -4,8 +4,10 @@
                     [--sparsity S] [--raster] [--no-cpu-baseline]
 
 One step is one pass of the whole path over one attention call of the
-workload: permute Q, K, V (3D windows), pool block means, predict the mask,
-block-sparse attention, unpermute O.  Inputs are synthetic (seeded) and
+workload: permute K and V (3D windows), pool the block means of Q and K,
+predict the mask, block-sparse attention reading Q and writing O in raster
+order (the fused path; --unfused permutes Q and unpermutes O in passes of
+their own, as the FP8 path does).  Inputs are synthetic (seeded) and
 resident in HBM before timing starts; every output buffer is allocated
 beforehand, so the timed region only launches kernels.
 
@@ -53,6 +55,11 @@ def parse():
     ap.add_argument("--raster", action="store_true",
                     help="permutation off (raster blocks)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="one JSON line per workload point (all configurations, the "
+                         "720p sparsity sweep in window and raster order)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="permute Q and unpermute O in passes of their own")
     ap.add_argument("--cpu-tiles", type=int, default=660,
                     help="query tiles in the oracle's attention sample")
     ap.add_argument("--cpu-heads", type=int, default=2,
@@ -284,7 +291,7 @@ def cpu_baseline(cfg, q, k, v, sparsity, n_tiles_sample, exec_flop_total, fp8=Fa
     heads and tiles (heads are independent and every video row keeps the
     same number of tiles)."""
     import numpy as np
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import rainfusion_oracle as orc
 
@@ -297,6 +304,9 @@ def cpu_baseline(cfg, q, k, v, sparsity, n_tiles_sample, exec_flop_total, fp8=Fa
     H = cfg.H * cfg.B
     n_heads = max(1, min(n_heads, cfg.H))
     fixed = attn = 0.0
+    host_cpus = len(os.sched_getaffinity(0))
+    # The oracle's matrix products use every host core this process may run on.
+    limiter = threadpool_limits(limits=host_cpus)
     for h in range(n_heads):
         f64 = lambda t: t[:1, h:h + 1].cpu().double().numpy()
         qh, kh, vh = f64(q), f64(k), f64(v)
@@ -320,10 +330,23 @@ def cpu_baseline(cfg, q, k, v, sparsity, n_tiles_sample, exec_flop_total, fp8=Fa
     per_tile = attn / (n_heads * len(tiles))
     full = H * per_head_fixed + H * z["n_tiles"] * per_tile
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    limiter.unregister()
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f
+                          if l.startswith("model name")), "")
+    except OSError:
+        pass
     return {
         "value": exec_flop_total / full / 1e12,
         "unit": "TFLOP/s",
+        # threads the oracle ran on: its BLAS products use them all; the
+        # permutation, pooling and selection loops run on one
         "cores": int(threads),
+        "host_cpus": host_cpus,
+        "nproc": os.cpu_count(),
+        "cpu_model": model,
         "kind": "oracle",
         "sample": (f"heads 0-{n_heads - 1} of {H}: permute, means, mask, unpermute in "
                    f"full; attention on {len(tiles)} of {z['n_tiles']} query tiles "
@@ -348,8 +371,10 @@ def main():
         return 2
     import torch
 
-    from image_diffusion_dits_amd import configs, inputs, rf
+    from image_diffusion_dits_amd import configs, inputs
 
+    if a.sweep:
+        return sweep(a)
     cfg = configs.get(a.config)
     if a.raster:
         cfg = configs.SWEEP_RASTER if a.config in (3, 5) else cfg
@@ -357,10 +382,74 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     q, k, v = inputs.make_qkv(cfg, dev)
+    rec, exec_flop = measure(a, cfg, s, q, k, v)
+    if not a.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(cfg, q, k, v, s, a.cpu_tiles, exec_flop, a.fp8,
+                                           a.cpu_heads)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def host_info():
+    """Host facts recorded beside each measurement."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f
+                          if l.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "host_cpus": len(os.sched_getaffinity(0)),
+            "cpu_model": model}
+
+
+def sweep(a):
+    """One JSON line per (workload, sparsity, order): the tiny fp32 case, the
+    image, the 720p and long+text videos at their sparsities, and the 720p
+    sweep over sparsity in window and raster order.  Each line carries the
+    sha256 of the inputs, so that it can be joined with the parity record of
+    the same point."""
+    import torch
+
+    from image_diffusion_dits_amd import configs, inputs
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    points = [(configs.TINY, 50), (configs.IMAGE, 60), (configs.VIDEO720, 80),
+              (configs.VIDEO_LONG, 85)]
+    points += [(configs.SWEEP, sp) for sp in configs.SWEEP.sparsity]
+    points += [(configs.SWEEP_RASTER, sp) for sp in configs.SWEEP_RASTER.sparsity]
+    host = host_info()
+    cache = {}
+    for cfg, sp in points:
+        key = (cfg.cid, cfg.permute)
+        if key not in cache:
+            cache.clear()
+            torch.cuda.empty_cache()
+            dev_in = "cpu" if cfg.cid in (1, 2) else dev
+            q, k, v = (t.to(dev) for t in inputs.make_qkv(cfg, dev_in))
+            cache[key] = (q, k, v, {n: inputs.sha256(t) for n, t in
+                                    (("q", q), ("k", k), ("v", v))})
+        q, k, v, sha = cache[key]
+        rec, _ = measure(a, cfg, sp, q, k, v)
+        rec["inputs_sha256"] = sha
+        rec["host"] = host
+        print(json.dumps(rec), flush=True)
+    return 0
+
+
+def measure(a, cfg, s, q, k, v):
+    """Times the step on one workload point; returns (record, executed FLOP
+    per call)."""
+    import torch
+
+    from image_diffusion_dits_amd import rf
+
+    dev = q.device
     plan = rf.Plan(cfg.layout)
     z = plan.sizes
     kc = plan.keep(s)
-    B, H, d = cfg.B, cfg.H, cfg.d
+    B, H, d = q.shape[0], q.shape[1], q.shape[3]
     bs = z["bs"]
 
     # Every buffer is allocated before timing.
@@ -380,8 +469,11 @@ def main():
         ks = torch.empty_like(qs)
         vs = torch.empty(B, H, d, dtype=torch.float32, device=dev)
 
+    fused = not (a.fp8 or a.unfused)
     if a.fp8:
         stages = ["permute_fp8_qk", "permute_fp8_v", "predict_mask", "sparse_attn", "unpermute"]
+    elif fused:
+        stages = ["means_q_permute_means_k", "permute_v", "predict_mask", "sparse_attn"]
     else:
         stages = ["permute_means_qk", "permute_v", "predict_mask", "sparse_attn", "unpermute"]
     n_ev = len(stages) + 1
@@ -399,6 +491,11 @@ def main():
             rf.permute_fp8(plan, k, means=True, out=k8, scale=ks, xbar=kbar)
             mark()
             rf.permute_fp8(plan, v, order=rf.TILES_T, out=v8, scale=vs)
+        elif fused:
+            rf.permute_means(plan, q, xbar=qbar, means_only=True)
+            rf.permute_means(plan, k, out=kp, xbar=kbar)
+            mark()
+            rf.permute(plan, v, order=rf.TILES_T, out=vt)
         else:
             rf.permute_means(plan, q, out=qp, xbar=qbar)
             rf.permute_means(plan, k, out=kp, xbar=kbar)
@@ -409,11 +506,14 @@ def main():
         mark()
         if a.fp8:
             rf.sparse_attn_fp8(plan, q8, qs, k8, ks, v8, vs, kept, s, out=op)
+        elif fused:
+            rf.sparse_attn_raster(plan, q, kp, vt, kept, s, out=o)
         else:
             rf.sparse_attn(plan, qp, kp, vt, kept, s, out=op)
         mark()
-        rf.unpermute(plan, op, out=o)
-        mark()
+        if not fused:
+            rf.unpermute(plan, op, out=o)
+            mark()
 
     for _ in range(a.warmup):
         step()
@@ -452,7 +552,7 @@ def main():
     else:
         peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
     attn_tflops = exec_flop / attn_s / 1e12
-    workload = cfg.name + ("" if cfg.permute else "-raster")
+    workload = cfg.name + ("" if cfg.permute or cfg.name.endswith("-raster") else "-raster")
     kernel = ("attn_fp8_pp_kernel" if a.fp8 else
               "attn_bf16_pp_kernel" if cfg.dtype == "bf16" else "attn_f32_kernel")
     traffic = stored_traffic(kernel, workload)
@@ -462,6 +562,7 @@ def main():
     unperm_bytes = B * H * 2 * z["L"] * d * esize
     perm8_bytes = B * H * (z["L"] * esize + z["Lt"]) * d      # bf16 in, e4m3 out
     perm8v_bytes = B * H * (2 * z["L"] * esize + z["Lt"]) * d  # maxima pass, then one pass
+    means_bytes = B * H * z["L"] * d * esize                   # read only
 
     rec = {
         "metric": METRIC,
@@ -477,7 +578,8 @@ def main():
         "dtype": "fp8" if a.fp8 else cfg.dtype,
         "data": "synthetic",
         "config": {
-            "workload": workload, "batch": B, "heads": H, "head_dim": d,
+            "workload": workload, "path": ("fp8" if a.fp8 else "fused" if fused else "five-pass"),
+            "batch": B, "heads": H, "head_dim": d,
             "tokens": z["N"], "text_tokens": z["L"] - z["N"],
             "padded_slots": z["Lp"], "block": bs, "blocks": z["nb"],
             "sparsity_pct": s, "kept_tiles_per_row": kc["k_eff"],
@@ -498,6 +600,10 @@ def main():
             "permute_fp8_v": round(perm8v_bytes / (stage_ms["permute_fp8_v"] / 1e3) / 1e9, 1),
             "unpermute": round(unperm_bytes / (stage_ms["unpermute"] / 1e3) / 1e9, 1),
         } if a.fp8 else {
+            "means_q_permute_means_k": round((means_bytes + perm_bytes) / (
+                stage_ms["means_q_permute_means_k"] / 1e3) / 1e9, 1),
+            "permute_v": round(perm_bytes / (stage_ms["permute_v"] / 1e3) / 1e9, 1),
+        } if fused else {
             "permute_means_qk": round(2 * perm_bytes / (stage_ms["permute_means_qk"] / 1e3) / 1e9, 1),
             "permute_v": round(perm_bytes / (stage_ms["permute_v"] / 1e3) / 1e9, 1),
             "unpermute": round(unperm_bytes / (stage_ms["unpermute"] / 1e3) / 1e9, 1),
@@ -536,12 +642,8 @@ def main():
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
         rec["copy_probe_bytes"] = {"read": 2 * n, "write": 2 * n}
-    if not a.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(cfg, q, k, v, s, a.cpu_tiles, exec_flop, a.fp8,
-                                           a.cpu_heads)
-    print(json.dumps(rec), flush=True)
     plan.close()
-    return 0
+    return rec, exec_flop
 
 
 if __name__ == "__main__":

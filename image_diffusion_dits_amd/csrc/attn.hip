@@ -43,6 +43,19 @@ typedef float f32x8 __attribute__((__vector_size__(8 * sizeof(float))));
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
 
+// Rows of the query operand, the output and the LSE.  slot_src == nullptr:
+// permuted tensors [BH][Lt][d] ([BH][Lt] for the LSE), query slot q at row q.
+// Otherwise raster tensors [BH][rows][d]: slot q reads and writes raster row
+// slot_src[q], and pad slots (slot_src < 0) read zeros and write nothing.
+struct RowIo {
+  const int32_t* slot_src;
+  int64_t rows;
+};
+
+__device__ inline int64_t io_row(const RowIo& io, int64_t slot) {
+  return io.slot_src != nullptr ? int64_t(io.slot_src[slot]) : slot;
+}
+
 // ---------------------------------------------------------------- bf16 MFMA
 
 typedef const __attribute__((address_space(1))) void global_cvoid;
@@ -100,7 +113,7 @@ template <int D, int BS>
 __global__ __launch_bounds__((BS / 32) * 64, 2) void attn_bf16_kernel(
     const __bf16* __restrict__ qp, const __bf16* __restrict__ kp,
     const __bf16* __restrict__ vt, const int32_t* __restrict__ kept,
-    __bf16* __restrict__ op, float* __restrict__ lse,
+    __bf16* __restrict__ op, float* __restrict__ lse, RowIo io,
     const uint32_t* __restrict__ tile_bits,
     const int32_t* __restrict__ tile_count, int64_t Lt, int32_t BH,
     int32_t nb, int32_t n_tt, int32_t row_len_video, int64_t nnz,
@@ -129,12 +142,13 @@ __global__ __launch_bounds__((BS / 32) * 64, 2) void attn_bf16_kernel(
 
   // Q operand (B of S^T = K Q^T): lane (li, g) holds q[li][16m + 8g .. +8].
   const int64_t qrow = int64_t(qtile) * BS + wave * 32 + li;
+  const int64_t iorow = io_row(io, qrow);
   bf16x8 qf[D / 16];
   {
-    const __bf16* qsrc = qp + (bh * Lt + qrow) * D + 8 * g;
+    const __bf16* qsrc = qp + (bh * io.rows + max(iorow, int64_t(0))) * D + 8 * g;
 #pragma unroll
     for (int m = 0; m < D / 16; ++m)
-      qf[m] = *reinterpret_cast<const bf16x8*>(qsrc + 16 * m);
+      qf[m] = iorow >= 0 ? *reinterpret_cast<const bf16x8*>(qsrc + 16 * m) : bf16x8{};
   }
 
   f32x16 o[D / 32];
@@ -152,6 +166,7 @@ __global__ __launch_bounds__((BS / 32) * 64, 2) void attn_bf16_kernel(
 #pragma unroll
   for (int u = 0; u < VCopy::kVariants; ++u) voff[u] = VCopy::lane_offset(wave, lane, u);
   auto load_k = [&](int32_t kt) {
+    poison_tile<C::kKLoads, C::kWaves>(ks, wave, lane);
     const char* base = kh + int64_t(kt) * BS * C::kKRowBytes;
 #pragma unroll
     for (int u = 0; u < C::kKLoads; ++u) {
@@ -162,6 +177,7 @@ __global__ __launch_bounds__((BS / 32) * 64, 2) void attn_bf16_kernel(
     }
   };
   auto load_v = [&](int32_t kt) {
+    poison_tile<C::kVLoads, C::kWaves>(vs, wave, lane);
     const char* base = vh + int64_t(kt) * D * C::kVRowBytes;
 #pragma unroll
     for (int u = 0; u < C::kVLoads; ++u) {
@@ -329,8 +345,9 @@ __global__ __launch_bounds__((BS / 32) * 64, 2) void attn_bf16_kernel(
   const int qs = wave * 32 + li;
   const bool qvalid = (tile_bits[qtile * 4 + qs / 32] >> (qs % 32)) & 1u;
   const float inv = (qvalid && l_tot > 0.f) ? 1.f / l_tot : 0.f;
-  if (lse != nullptr && g == 0) lse[bh * Lt + qrow] = lse_of(m_run, l_tot, qvalid);
-  __bf16* dst = op + (bh * Lt + qrow) * D + 4 * g;
+  if (iorow < 0) return;                      // pad slot of a raster output
+  if (lse != nullptr && g == 0) lse[bh * io.rows + iorow] = lse_of(m_run, l_tot, qvalid);
+  __bf16* dst = op + (bh * io.rows + iorow) * D + 4 * g;
   typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
@@ -374,7 +391,7 @@ template <int D>
 __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
     const __bf16* __restrict__ qp, const __bf16* __restrict__ kp,
     const __bf16* __restrict__ vt, const int32_t* __restrict__ kept,
-    __bf16* __restrict__ op, float* __restrict__ lse,
+    __bf16* __restrict__ op, float* __restrict__ lse, RowIo io,
     const uint32_t* __restrict__ tile_bits,
     const int32_t* __restrict__ tile_count, int64_t Lt, int32_t BH,
     int32_t nb, int32_t n_tt, int32_t row_len_video, int64_t nnz,
@@ -416,10 +433,11 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
   const int64_t qrow = int64_t(qtile) * BS + qw * 32 + li;
   bf16x8 qf[D / 16];
   {
-    const __bf16* qsrc = qp + (bh * Lt + qrow) * D + 8 * g;
+    const int64_t iorow = io_row(io, qrow);
+    const __bf16* qsrc = qp + (bh * io.rows + max(iorow, int64_t(0))) * D + 8 * g;
 #pragma unroll
     for (int m = 0; m < D / 16; ++m)
-      qf[m] = *reinterpret_cast<const bf16x8*>(qsrc + 16 * m);
+      qf[m] = iorow >= 0 ? *reinterpret_cast<const bf16x8*>(qsrc + 16 * m) : bf16x8{};
   }
   f32x16 o[D / 32];
 #pragma unroll
@@ -509,13 +527,24 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
     }
   };
 
+  // Per-tile scalars of this group's walk, carried in SGPRs: the kept tiles
+  // of steps i and i + 1 and the validity words of step i.  Each VALU phase
+  // loads those of the next step early on, so that the phase after it
+  // starts without waiting on scalar memory.  A tile is full when its four
+  // validity words are all ones.
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const __attribute__((address_space(4))) u32x4* tbits4 =
+      (const __attribute__((address_space(4))) u32x4*)tile_bits;
+  int32_t kt_cur = tile_of(0), kt_nxt = tile_of(1);
+  u32x4 bits_cur = tbits4[max(kt_cur, 0)];
+
   // VALU phase of tile i: the copies of K(i+1) and V^T(i) (their buffers
   // were last read in the MFMA phase just finished) and softmax(i).
   auto valu_phase = [&](int32_t i) {
     if (i < 0 || i >= n_grp) return;
-    const int32_t kt = tile_of(i);
+    const int32_t kt = kt_cur;
     const bool next_k = i + 1 < n_grp;
-    const TileCopy<C::kGroupWaves> ck(kh + int64_t(max(next_k ? tile_of(i + 1) : 0, 0)) *
+    const TileCopy<C::kGroupWaves> ck(kh + int64_t(max(next_k ? kt_nxt : 0, 0)) *
                                           C::kTileBytes, C::kTileBytes, ks, koff, qw);
     const TileCopy<C::kGroupWaves> cv(vh + int64_t(max(kt, 0)) * C::kTileBytes, C::kTileBytes,
                                       vsg, voff, qw);
@@ -534,8 +563,14 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
+    if (next_k) poison_tile<C::kCopies, C::kGroupWaves>(ks, qw, lane);
+    poison_tile<C::kCopies, C::kGroupWaves>(vsg, qw, lane);
     copies(I0{});
-    const int32_t tcount = kt >= 0 ? tile_count[kt] : 0;
+    // The next step's scalars (in flight during the softmax).
+    const int32_t kt_n2 = tile_of(i + 2);
+    const u32x4 bits_n = tbits4[max(kt_nxt, 0)];
+    const u32x4 bits = kt >= 0 ? bits_cur : u32x4{0u, 0u, 0u, 0u};
+    const bool partial = (bits.x & bits.y & bits.z & bits.w) != 0xFFFFFFFFu;
     // Row max over the tile (raw dot products; the scale is positive).
     auto row_max = [&]() {
       float m = -INFINITY;
@@ -556,12 +591,13 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
     // weights are taken out of the row sum afterwards.  Otherwise (and for a
     // masked tile, kt < 0, whose copies hold tile 0) they are set to -inf.
     bool pads_in_sum = false;
-    if (tcount != BS) {
+    if (partial) {
       if (kt < 0 || __ballot(!(mx > 0.f)) != 0) {
         // Keys of lane group g sit at bit 8g + (16(a/2) + 4(a%2) + b).
 #pragma unroll
         for (int kb = 0; kb < BS / 32; ++kb) {
-          const uint32_t bits = (kt >= 0 ? tile_bits[kt * 4 + kb] : 0u) >> (8 * g);
+          const uint32_t word = kb == 0 ? bits.x : kb == 1 ? bits.y : kb == 2 ? bits.z : bits.w;
+          const uint32_t bits = word >> (8 * g);
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int a = r / 4, b = r % 4;
@@ -625,19 +661,34 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
       // Each pad key of this lane's half of the tile (bits 8g + {0..7,
       // 16..23} of each validity word) scored exactly 0 and so got the
       // weight 2^(0 - m).
-      uint32_t npad = 0;
-#pragma unroll
-      for (int kb = 0; kb < BS / 32; ++kb)
-        npad += __popc(~tile_bits[kt * 4 + kb] & (g ? 0xFF00FF00u : 0x00FF00FFu));
+      const uint32_t half = g ? 0xFF00FF00u : 0x00FF00FFu;
+      const uint32_t npad = __popc(~bits.x & half) + __popc(~bits.y & half) +
+                            __popc(~bits.z & half) + __popc(~bits.w & half);
       lsum -= float(npad) * __builtin_amdgcn_exp2f(neg_m);
     }
     l_run = lsum;
     // The wait stays after the softmax, which it would otherwise precede.
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);   // the copies have landed
+    // The next step's scalars have arrived too (forced here, before the
+    // barrier, so that no scalar load is in flight during the MFMA phase,
+    // where it would coarsen the LDS waits).
+    asm volatile("" ::"s"(kt_n2), "s"(bits_n.x), "s"(bits_n.y), "s"(bits_n.z),
+                 "s"(bits_n.w));
+    kt_cur = kt_nxt;
+    kt_nxt = kt_n2;
+    bits_cur = bits_n;
   };
 
-  if (n_grp > 0) copy_k(tile_of(0));
+  if (n_grp > 0) {
+    poison_tile<C::kCopies, C::kGroupWaves>(ks, qw, lane);
+    copy_k(kt_cur);
+  }
+  // Every scalar the loop reads is resident before it starts: a scalar load
+  // still pending at the loop entry would make the compiler wait on all LDS
+  // reads at once (lgkmcnt(0)) at the start of each MFMA phase.
+  asm volatile("" ::"s"(kt_nxt), "s"(bits_cur.x), "s"(bits_cur.y), "s"(bits_cur.z),
+               "s"(bits_cur.w), "s"(scale_log2), "s"(n_grp), "s"(row_len));
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __builtin_amdgcn_s_barrier();
   // Phase pairs: group 0 runs MFMA(i) then VALU(i); group 1 runs VALU(i-1)
@@ -689,9 +740,11 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
   const bool qvalid = (tile_bits[qtile * 4 + qs / 32] >> (qs % 32)) & 1u;
   const float inv = (qvalid && l_tot > 0.f) ? 1.f / l_tot : 0.f;
   const float ca = fa * inv, cb = fb * inv;
-  if (lse != nullptr && g == 0) lse[bh * Lt + qrow] = lse_of(m_t, l_tot, qvalid);
+  const int64_t iorow = io_row(io, qrow);
+  if (iorow < 0) return;                      // pad slot of a raster output
+  if (lse != nullptr && g == 0) lse[bh * io.rows + iorow] = lse_of(m_t, l_tot, qvalid);
   // Lane (li, g) holds O^T[dd = db*32 + 8a + 4g + b][query li].
-  __bf16* dst = op + (bh * Lt + qrow) * D + 4 * g;
+  __bf16* dst = op + (bh * io.rows + iorow) * D + 4 * g;
   typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
@@ -711,7 +764,7 @@ template <int D, int BS>
 __global__ __launch_bounds__(BS) void attn_f32_kernel(
     const float* __restrict__ qp, const float* __restrict__ kp,
     const float* __restrict__ vt, const int32_t* __restrict__ kept,
-    float* __restrict__ op, float* __restrict__ lse,
+    float* __restrict__ op, float* __restrict__ lse, RowIo io,
     const uint32_t* __restrict__ tile_bits,
     const int32_t* __restrict__ tile_count, int64_t Lt, int32_t BH,
     int32_t nb, int32_t n_tt, int32_t row_len_video, int64_t nnz,
@@ -731,10 +784,11 @@ __global__ __launch_bounds__(BS) void attn_f32_kernel(
   const int32_t* row = kept + bh * nnz + rr.offset;
   const int32_t row_len = rr.len;
 
+  const int64_t iorow = io_row(io, qrow);
   float q[D], o[D];
 #pragma unroll
   for (int c = 0; c < D; ++c) {
-    q[c] = qp[(bh * Lt + qrow) * D + c];
+    q[c] = iorow >= 0 ? qp[(bh * io.rows + iorow) * D + c] : 0.f;
     o[c] = 0.f;
   }
   float m_run = -INFINITY, l_run = 0.f;
@@ -786,23 +840,24 @@ __global__ __launch_bounds__(BS) void attn_f32_kernel(
   }
   const bool qvalid = (tile_bits[qtile * 4 + t / 32] >> (t % 32)) & 1u;
   const float inv = (qvalid && l_run > 0.f) ? 1.f / l_run : 0.f;
+  if (iorow < 0) return;                      // pad slot of a raster output
   if (lse != nullptr)
-    lse[bh * Lt + qrow] = (qvalid && l_run > 0.f) ? m_run + logf(l_run) : -INFINITY;
-  float* dst = op + (bh * Lt + qrow) * D;
+    lse[bh * io.rows + iorow] = (qvalid && l_run > 0.f) ? m_run + logf(l_run) : -INFINITY;
+  float* dst = op + (bh * io.rows + iorow) * D;
 #pragma unroll
   for (int c = 0; c < D; ++c) dst[c] = o[c] * inv;
 }
 
 template <int D, int BS>
 void launch_bf16(const rf_plan* p, const void* qp, const void* kp,
-                 const void* vt, const int32_t* kept, void* op, float* lse, int BH,
-                 int32_t row_len_video, int64_t nnz, float scale, hipStream_t st) {
+                 const void* vt, const int32_t* kept, void* op, float* lse, RowIo io,
+                 int BH, int32_t row_len_video, int64_t nnz, float scale, hipStream_t st) {
   const int nb = p->sz.nb, n_tt = p->sz.n_text_tiles;
   dim3 grid(BH * (nb + n_tt));
   if constexpr (BS == 128) {
     hipLaunchKernelGGL((attn_bf16_pp_kernel<D>), grid, dim3(PpCfg<D>::kThreads), 0, st,
                        static_cast<const __bf16*>(qp), static_cast<const __bf16*>(kp),
-                       static_cast<const __bf16*>(vt), kept, static_cast<__bf16*>(op), lse,
+                       static_cast<const __bf16*>(vt), kept, static_cast<__bf16*>(op), lse, io,
                        p->tile_bits, p->tile_count, p->sz.Lt, BH, nb, n_tt,
                        row_len_video, nnz,
                        scale * 1.4426950408889634f);
@@ -811,7 +866,7 @@ void launch_bf16(const rf_plan* p, const void* qp, const void* kp,
   hipLaunchKernelGGL((attn_bf16_kernel<D, BS>), grid,
                      dim3(Bf16Cfg<D, BS>::kThreads), 0, st,
                      static_cast<const __bf16*>(qp), static_cast<const __bf16*>(kp),
-                     static_cast<const __bf16*>(vt), kept, static_cast<__bf16*>(op), lse,
+                     static_cast<const __bf16*>(vt), kept, static_cast<__bf16*>(op), lse, io,
                      p->tile_bits, p->tile_count, p->sz.Lt, BH, nb, n_tt,
                      row_len_video, nnz,
                      scale * 1.4426950408889634f);
@@ -819,13 +874,13 @@ void launch_bf16(const rf_plan* p, const void* qp, const void* kp,
 
 template <int D, int BS>
 void launch_f32(const rf_plan* p, const void* qp, const void* kp,
-                const void* vt, const int32_t* kept, void* op, float* lse, int BH,
-                int32_t row_len_video, int64_t nnz, float scale, hipStream_t st) {
+                const void* vt, const int32_t* kept, void* op, float* lse, RowIo io,
+                int BH, int32_t row_len_video, int64_t nnz, float scale, hipStream_t st) {
   const int nb = p->sz.nb, n_tt = p->sz.n_text_tiles;
   dim3 grid(BH * (nb + n_tt));
   hipLaunchKernelGGL((attn_f32_kernel<D, BS>), grid, dim3(BS), 0, st,
                      static_cast<const float*>(qp), static_cast<const float*>(kp),
-                     static_cast<const float*>(vt), kept, static_cast<float*>(op), lse,
+                     static_cast<const float*>(vt), kept, static_cast<float*>(op), lse, io,
                      p->tile_bits, p->tile_count, p->sz.Lt, BH, nb, n_tt,
                      row_len_video, nnz, scale);
 }
@@ -836,7 +891,7 @@ rf_status sparse_attn(const rf_plan* plan, const void* qp, const void* kp,
                       const void* vt, const int32_t* kept_idx,
                       int32_t row_len_video, int64_t nnz, void* op, float* lse, int32_t B,
                       int32_t H, int32_t d, float scale, rf_dtype dtype,
-                      hipStream_t stream, const char* fn) {
+                      hipStream_t stream, const char* fn, bool raster = false) {
   rf_status st = rf::check_call(plan, B, H, d, dtype, fn);
   if (st != RF_OK) return st;
   if (!rf::aligned16(qp) || !rf::aligned16(kp) || !rf::aligned16(vt) ||
@@ -851,16 +906,17 @@ rf_status sparse_attn(const rf_plan* plan, const void* qp, const void* kp,
     return rf::fail(RF_ERR_UNSUPPORTED, "%s: too many tiles", fn);
   const int bs = plan->sz.bs;
   const int32_t rl = row_len_video;
+  const RowIo io = raster ? RowIo{plan->slot_src, plan->sz.L} : RowIo{nullptr, plan->sz.Lt};
   if (dtype == RF_BF16) {
-    if (d == 128 && bs == 128) launch_bf16<128, 128>(plan, qp, kp, vt, kept_idx, op, lse, BH, rl, nnz, scale, stream);
-    else if (d == 128 && bs == 64) launch_bf16<128, 64>(plan, qp, kp, vt, kept_idx, op, lse, BH, rl, nnz, scale, stream);
-    else if (d == 64 && bs == 128) launch_bf16<64, 128>(plan, qp, kp, vt, kept_idx, op, lse, BH, rl, nnz, scale, stream);
-    else launch_bf16<64, 64>(plan, qp, kp, vt, kept_idx, op, lse, BH, rl, nnz, scale, stream);
+    if (d == 128 && bs == 128) launch_bf16<128, 128>(plan, qp, kp, vt, kept_idx, op, lse, io, BH, rl, nnz, scale, stream);
+    else if (d == 128 && bs == 64) launch_bf16<128, 64>(plan, qp, kp, vt, kept_idx, op, lse, io, BH, rl, nnz, scale, stream);
+    else if (d == 64 && bs == 128) launch_bf16<64, 128>(plan, qp, kp, vt, kept_idx, op, lse, io, BH, rl, nnz, scale, stream);
+    else launch_bf16<64, 64>(plan, qp, kp, vt, kept_idx, op, lse, io, BH, rl, nnz, scale, stream);
   } else {
-    if (d == 128 && bs == 128) launch_f32<128, 128>(plan, qp, kp, vt, kept_idx, op, lse, BH, rl, nnz, scale, stream);
-    else if (d == 128 && bs == 64) launch_f32<128, 64>(plan, qp, kp, vt, kept_idx, op, lse, BH, rl, nnz, scale, stream);
-    else if (d == 64 && bs == 128) launch_f32<64, 128>(plan, qp, kp, vt, kept_idx, op, lse, BH, rl, nnz, scale, stream);
-    else launch_f32<64, 64>(plan, qp, kp, vt, kept_idx, op, lse, BH, rl, nnz, scale, stream);
+    if (d == 128 && bs == 128) launch_f32<128, 128>(plan, qp, kp, vt, kept_idx, op, lse, io, BH, rl, nnz, scale, stream);
+    else if (d == 128 && bs == 64) launch_f32<128, 64>(plan, qp, kp, vt, kept_idx, op, lse, io, BH, rl, nnz, scale, stream);
+    else if (d == 64 && bs == 128) launch_f32<64, 128>(plan, qp, kp, vt, kept_idx, op, lse, io, BH, rl, nnz, scale, stream);
+    else launch_f32<64, 64>(plan, qp, kp, vt, kept_idx, op, lse, io, BH, rl, nnz, scale, stream);
   }
   return rf::check_launch(fn);
 }
@@ -880,6 +936,24 @@ extern "C" rf_status rf_sparse_attn(const rf_plan* plan, const void* qp,
   if (st != RF_OK) return st;
   return sparse_attn(plan, qp, kp, vt, kept_idx, kc.row_len_video, kc.nnz_per_head,
                      op, lse_or_null, B, H, d, scale, dtype, stream, "rf_sparse_attn");
+}
+
+extern "C" rf_status rf_sparse_attn_raster(const rf_plan* plan, const void* q,
+                                           const void* kp, const void* vt,
+                                           const int32_t* kept_idx,
+                                           int32_t sparsity_pct, void* o,
+                                           float* lse_or_null, int32_t B, int32_t H,
+                                           int32_t d, float scale, rf_dtype dtype,
+                                           hipStream_t stream) {
+  if (plan == nullptr) return rf::fail(RF_ERR_INVALID_ARG, "rf_sparse_attn_raster: null plan");
+  rf_keep kc;
+  rf_status st = rf_layout_keep(&plan->lay, sparsity_pct, &kc);
+  if (st != RF_OK) return st;
+  if (q == o && q != nullptr)
+    return rf::fail(RF_ERR_INVALID_ARG, "rf_sparse_attn_raster: q and o must not overlap");
+  return sparse_attn(plan, q, kp, vt, kept_idx, kc.row_len_video, kc.nnz_per_head, o,
+                     lse_or_null, B, H, d, scale, dtype, stream, "rf_sparse_attn_raster",
+                     true);
 }
 
 extern "C" rf_status rf_sparse_attn_rows(const rf_plan* plan, const void* qp,

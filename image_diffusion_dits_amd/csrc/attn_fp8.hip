@@ -190,12 +190,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
     return a;
   };
 
-  // Validity word w + g of tile kt (0 for a masked tile), read as two
-  // uniform scalar loads: a per-lane vector load would have to wait, in
-  // order, for every tile copy issued before it.
-  auto tile_word = [&](int32_t kt, int w) -> uint32_t {
-    if (kt < 0) return 0u;
-    const uint32_t w0 = tile_bits[kt * 4 + w], w1 = tile_bits[kt * 4 + w + 1];
+  // Per-tile scalars of this group's walk, carried in SGPRs: the kept tiles
+  // of steps i and i + 1, the validity words and the K scale of step i.
+  // Each VALU phase loads those of the next step early on (uniform scalar
+  // loads: a per-lane vector load would wait, in order, for every tile copy
+  // issued before it), so that no phase starts waiting on scalar memory.
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const __attribute__((address_space(4))) u32x4* tbits4 =
+      (const __attribute__((address_space(4))) u32x4*)tile_bits;
+  const __attribute__((address_space(4))) float* kscale =
+      (const __attribute__((address_space(4))) float*)ksc;
+  int32_t kt_cur = tile_of(0), kt_nxt = tile_of(1);
+  u32x4 bits_cur = tbits4[max(kt_cur, 0)];
+  float ks_cur = kscale[max(kt_cur, 0)];
+  // Validity word w + g of the current tile (0 for a masked tile).
+  auto tile_word = [&](const u32x4& b, int w) -> uint32_t {
+    const uint32_t w0 = w == 0 ? b.x : b.z, w1 = w == 0 ? b.y : b.w;
     return g ? w1 : w0;
   };
 
@@ -230,20 +240,27 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
       // this phase's LDS reads: their issue stalls fall in the wait at the
       // barrier, and the group's VALU phase waits for them at its end.
       __builtin_amdgcn_sched_barrier(0);
-      const int32_t kt = tile_of(i);
-      if (i + 1 < n_grp) copy_k(tile_of(i + 1), (i + 1) & 1);
-      copy_v(kt, i & 1);
+      if (i + 1 < n_grp) {
+        poison_tile<kCopies, kGroupWaves>(kslot + ((i + 1) & 1) * kTileBytes, qw, lane);
+        copy_k(kt_nxt, (i + 1) & 1);
+      }
+      poison_tile<kCopies, kGroupWaves>(vslot + (i & 1) * kTileBytes, qw, lane);
+      copy_v(kt_cur, i & 1);
     }
   };
 
   auto valu_phase = [&](int32_t i) {
     if (i < 0 || i >= n_grp) return;
-    const int32_t kt = tile_of(i);
-    const int32_t tcount = kt >= 0 ? tile_count[kt] : 0;
-    const float c = c_q * (kt >= 0 ? ksc[kt] : 1.f);
-    vw_full = tcount == BS;
+    const int32_t kt = kt_cur;
+    // The next step's scalars (in flight during the softmax).
+    const int32_t kt_n2 = tile_of(i + 2);
+    const u32x4 bits_n = tbits4[max(kt_nxt, 0)];
+    const float ks_n = kscale[max(kt_nxt, 0)];
+    const u32x4 bits = kt >= 0 ? bits_cur : u32x4{0u, 0u, 0u, 0u};
+    const float c = c_q * (kt >= 0 ? ks_cur : 1.f);
+    vw_full = (bits.x & bits.y & bits.z & bits.w) == 0xFFFFFFFFu;
 #pragma unroll
-    for (int st = 0; st < 2; ++st) vw[st] = tile_word(kt, 2 * st);
+    for (int st = 0; st < 2; ++st) vw[st] = tile_word(bits, 2 * st);
     // Row max over the tile's raw dot products (the scale is positive).
     auto row_max = [&]() {
       float m = -INFINITY;
@@ -263,13 +280,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
     // 2^(kRescale + kShift) = 2^8 (see below), so the pads need no mask.
     // Otherwise (and for a masked tile, kt < 0, whose copies hold tile 0)
     // they are set to -inf.
-    if (tcount != BS && (kt < 0 || __ballot(!(mx > 0.f)) != 0)) {
+    if (!vw_full && (kt < 0 || __ballot(!(mx > 0.f)) != 0)) {
       // Register r of block kb in lane group g is key 64(kb/2) + 32g +
       // 16(kb%2) + r: validity word 2(kb/2) + g, bit 16(kb%2) + r.
 #pragma unroll
       for (int kb = 0; kb < BS / 32; ++kb) {
         const uint32_t pad =
-            ~(tile_word(kt, 2 * (kb / 2)) >> (16 * (kb % 2)));
+            ~(tile_word(bits, 2 * (kb / 2)) >> (16 * (kb % 2)));
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const uint32_t m = uint32_t(int32_t(pad << (31 - r)) >> 31);
@@ -306,9 +323,26 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
       }
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);   // the copies have landed
+    // The next step's scalars have arrived too (forced here, before the
+    // barrier, so that no scalar load is in flight during the MFMA phase,
+    // where it would coarsen the LDS waits).
+    asm volatile("" ::"s"(kt_n2), "s"(bits_n.x), "s"(bits_n.y), "s"(bits_n.z),
+                 "s"(bits_n.w), "s"(ks_n));
+    kt_cur = kt_nxt;
+    kt_nxt = kt_n2;
+    bits_cur = bits_n;
+    ks_cur = ks_n;
   };
 
-  if (n_grp > 0) copy_k(tile_of(0), 0);
+  if (n_grp > 0) {
+    poison_tile<kCopies, kGroupWaves>(kslot, qw, lane);
+    copy_k(kt_cur, 0);
+  }
+  // Every scalar the loop reads is resident before it starts (a scalar load
+  // pending at the loop entry would coarsen the LDS waits of every phase).
+  asm volatile("" ::"s"(kt_nxt), "s"(bits_cur.x), "s"(bits_cur.y), "s"(bits_cur.z),
+               "s"(bits_cur.w), "s"(ks_cur), "s"(scale_log2), "s"(c_q), "s"(n_grp),
+               "s"(row_len));
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __builtin_amdgcn_s_barrier();
   if (grp == 0) {

@@ -165,7 +165,8 @@ __global__ __launch_bounds__(kThreads) void permute_means_kernel(
   const int64_t bh = blockIdx.y;
   const int32_t tile = blockIdx.x;
   const uint8_t* src = x + bh * L * (D * E);
-  uint8_t* dst = xp + (bh * Lt + int64_t(tile) * BS) * (D * E);
+  // xp == nullptr: the means only (no permuted rows are written).
+  uint8_t* dst = xp != nullptr ? xp + (bh * Lt + int64_t(tile) * BS) * (D * E) : nullptr;
   const int k = threadIdx.x % CPR, rg = threadIdx.x / CPR;
   float acc[VE];
 #pragma unroll
@@ -182,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void permute_means_kernel(
 #pragma unroll
   for (int i = 0; i < BS / RG; ++i) {
     const int s = rg + i * RG;
-    store_nt(dst + int64_t(s) * (D * E) + k * 16, v[i]);
+    if (xp != nullptr) store_nt(dst + int64_t(s) * (D * E) + k * 16, v[i]);
     // Pad slots hold zeros here, so summing every slot sums the valid ones.
     if constexpr (E == 2) {
       const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
@@ -213,7 +214,8 @@ __global__ __launch_bounds__(kThreads) void permute_means_kernel(
 template <int E, int D, int BS>
 void launch_means(const rf_plan* p, const void* x, void* xp, float* xbar,
                   int BH, hipStream_t st) {
-  dim3 grid(p->sz.n_tiles, BH);
+  // Without permuted rows the text tiles have nothing to do.
+  dim3 grid(xp != nullptr ? p->sz.n_tiles : p->sz.nb, BH);
   hipLaunchKernelGGL((permute_means_kernel<E, D, BS>), grid, dim3(kThreads), 0, st,
                      static_cast<const uint8_t*>(x), static_cast<uint8_t*>(xp),
                      xbar, p->slot_src, p->tile_count, p->sz.L, p->sz.Lt,
@@ -271,7 +273,7 @@ rf_status rf_permute_means(const rf_plan* plan, const void* x, void* xp,
                            rf_dtype dtype, hipStream_t stream) {
   rf_status st = rf::check_call(plan, B, H, d, dtype, "rf_permute_means");
   if (st != RF_OK) return st;
-  if (!rf::aligned16(x) || !rf::aligned16(xp) || !rf::aligned16(xbar))
+  if (!rf::aligned16(x) || (xp != nullptr && !rf::aligned16(xp)) || !rf::aligned16(xbar))
     return rf::fail(RF_ERR_INVALID_ARG, "rf_permute_means: null or misaligned buffer");
   const int BH = B * H;
   const int bs = plan->sz.bs;

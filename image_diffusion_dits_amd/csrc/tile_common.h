@@ -133,6 +133,27 @@ __device__ __forceinline__ void dma_tile_perm(const char* base, int bytes, void*
         soff[u], 0, 0);
 }
 
+// Debug build (-DRF_POISON_LDS): before a wave's tile copy lands, the LDS
+// bytes that copy will overwrite (copy u of group wave w writes
+// [dst + (u*WAVES + w) * 1024, +1024)) are filled with 0x7fff halves, a NaN
+// as bf16 and NaN bytes as e4m3, and the fill is waited for, so it is in
+// LDS before the copy is issued.  An operand read that is not ordered after
+// its copy then returns NaN instead of stale numbers and fails parity.  In
+// the normal build this does nothing.
+template <int COPIES, int WAVES>
+__device__ __forceinline__ void poison_tile(void* dst, int w, int lane) {
+#ifdef RF_POISON_LDS
+  const uint4 nan = make_uint4(0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu);
+  char* d = static_cast<char*>(dst) + w * 1024 + lane * 16;
+#pragma unroll
+  for (int u = 0; u < COPIES; ++u)
+    *reinterpret_cast<uint4*>(d + u * WAVES * 1024) = nan;
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the fill is in LDS
+#else
+  (void)dst; (void)w; (void)lane;
+#endif
+}
+
 // Natural-log softmax normaliser of one query from the reference maximum m
 // (log2 units of the scaled logits) and the weight sum l taken relative to
 // it: ln sum_j exp(logit_j) = (m + log2 l) ln 2.  -inf for a pad query or a

@@ -69,10 +69,10 @@ class SparseAttention:
         self.shape = (B, H, z["L"], d)
         Lt, nt, bs = z["Lt"], z["n_tiles"], z["bs"]
         mk = dict(dtype=dtype, device=device)
-        self.qp = torch.empty(B, H, Lt, d, **mk)
+        # Q is read and O written in raster order by the attention call
+        # itself, so only K and V are held permuted.
         self.kp = torch.empty(B, H, Lt, d, **mk)
         self.vt = torch.empty(B, H, nt, d, bs, **mk)
-        self.op = torch.empty(B, H, Lt, d, **mk)
         self.qbar = torch.empty(B, H, z["nb"], d, dtype=torch.float32, device=device)
         self.kbar = torch.empty_like(self.qbar)
         s = policy.sparsity_pct
@@ -87,7 +87,7 @@ class SparseAttention:
         if tuple(q.shape) != self.shape:
             raise ValueError(f"expected {self.shape}, got {tuple(q.shape)}")
         mode = self.policy.mode(step)
-        rf.permute_means(self.plan, q, out=self.qp, xbar=self.qbar)
+        rf.permute_means(self.plan, q, xbar=self.qbar, means_only=True)
         rf.permute_means(self.plan, k, out=self.kp, xbar=self.kbar)
         rf.permute(self.plan, v, order=rf.TILES_T, out=self.vt)
         if mode == "dense":
@@ -101,8 +101,7 @@ class SparseAttention:
                                 self.policy.sparsity_pct, kept=self.kept)
                 self._have_mask = True
             kept, s = self.kept, self.policy.sparsity_pct
-        rf.sparse_attn(self.plan, self.qp, self.kp, self.vt, kept, s, out=self.op)
-        return rf.unpermute(self.plan, self.op, out=out)
+        return rf.sparse_attn_raster(self.plan, q, self.kp, self.vt, kept, s, out=out)
 
     def close(self):
         self.plan.close()

@@ -13,7 +13,9 @@ import os
 import numpy as np
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librf.so")
+# RF_LIB selects another build of the library (the debug builds of build.py).
+LIB_PATH = os.environ.get("RF_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "librf.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_BUFFER_TOO_SMALL = range(5)
 F32, BF16 = 0, 1
@@ -74,6 +76,8 @@ _SIGNATURES = {
                         _vp, _vp, _vp],
     "rf_sparse_attn": [_vp, _vp, _vp, _vp, _vp, _c_i32, _vp, _vp, _c_i32,
                        _c_i32, _c_i32, _c_f32, ctypes.c_int, _vp],
+    "rf_sparse_attn_raster": [_vp, _vp, _vp, _vp, _vp, _c_i32, _vp, _vp, _c_i32,
+                              _c_i32, _c_i32, _c_f32, ctypes.c_int, _vp],
     "rf_attention_recall": [_vp, _vp, _vp, _vp, _c_i32, _vp, _c_i32, _c_i32,
                             _c_i32, _c_i32, _c_f32, ctypes.c_int, _vp, _vp],
     "rf_tile_rank": [_P(Layout), _vp, _c_i64],
@@ -349,23 +353,26 @@ def permute(plan, x, order=ROWS, out=None):
     return out
 
 
-def permute_means(plan, x, out=None, xbar=None):
-    """Permuted rows of x (RF_ROWS) and the block means, in one pass."""
+def permute_means(plan, x, out=None, xbar=None, means_only=False):
+    """Permuted rows of x (RF_ROWS) and the block means, in one pass.  With
+    means_only=True no permuted rows are written and only xbar is returned."""
     B, H, d = _bhd(x)
     z = plan.sizes
     if x.shape[2] != z["L"]:
         raise ValueError(f"x has {x.shape[2]} tokens, layout needs {z['L']}")
-    if out is None:
+    if out is None and not means_only:
         out = torch.empty(B, H, z["Lt"], d, dtype=x.dtype, device=x.device)
     if xbar is None:
         xbar = torch.empty(B, H, z["nb"], d, dtype=torch.float32, device=x.device)
     _need(x, "x", (B, H, z["L"], d), _FLOAT)
-    _need(out, "out", (B, H, z["Lt"], d), (x.dtype,))
+    if not means_only:
+        _need(out, "out", (B, H, z["Lt"], d), (x.dtype,))
     _need(xbar, "xbar", (B, H, z["nb"], d), _F32)
-    _check(lib().rf_permute_means(plan.handle, _ptr(x), _ptr(out), _ptr(xbar), B,
+    _check(lib().rf_permute_means(plan.handle, _ptr(x),
+                                  None if means_only else _ptr(out), _ptr(xbar), B,
                                   H, d, _dtype_code(x), _stream()),
            "rf_permute_means")
-    return out, xbar
+    return xbar if means_only else (out, xbar)
 
 
 def unpermute(plan, xp, out=None):
@@ -451,6 +458,30 @@ def sparse_attn(plan, qp, kp, vt, kept, sparsity_pct, scale=None, out=None,
                                 _ptr(lo) if lse else None, B, H,
                                 d, float(scale), _dtype_code(qp), _stream()),
            "rf_sparse_attn")
+    return (out, lo) if lse else out
+
+
+def sparse_attn_raster(plan, q, kp, vt, kept, sparsity_pct, scale=None, out=None,
+                       lse=False):
+    """rf_sparse_attn_raster: raster q [B, H, L, d] in, raster O [B, H, L, d]
+    out (and with lse=True the fp32 log-sum-exp [B, H, L], raster order)."""
+    B, H, d = _bhd(q)
+    z = plan.sizes
+    _need(q, "q", (B, H, z["L"], d), _FLOAT)
+    _need(kp, "kp", (B, H, z["Lt"], d), (q.dtype,))
+    _vt_operand(plan, vt, B, H, d, (q.dtype,))
+    _kept_operand(plan, kept, B, H, sparsity_pct)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.shape, (q.dtype,))
+    lo = torch.empty(B, H, z["L"], dtype=torch.float32, device=q.device) if lse else None
+    _check(lib().rf_sparse_attn_raster(plan.handle, _ptr(q), _ptr(kp), _ptr(vt),
+                                       _ptr(kept), int(sparsity_pct), _ptr(out),
+                                       _ptr(lo) if lse else None, B, H, d, float(scale),
+                                       _dtype_code(q), _stream()),
+           "rf_sparse_attn_raster")
     return (out, lo) if lse else out
 
 
@@ -744,12 +775,19 @@ def kept_rows(plan, kept, sparsity_pct):
     return rows
 
 
-def sparse_attention(q, k, v, plan, sparsity_pct, scale=None):
+def sparse_attention(q, k, v, plan, sparsity_pct, scale=None, fused=True):
     """The whole path on raster tensors [B, H, N + n_text, d]: permute,
-    pool, predict, attend, unpermute.  Returns (o, kept)."""
-    qp, qbar = permute_means(plan, q)
+    pool, predict, attend, unpermute.  Returns (o, kept).  fused=True reads
+    Q and writes O in raster order inside the attention call (the query
+    means come from a means-only pass); fused=False permutes Q and
+    unpermutes O in passes of their own.  Both give the same bytes."""
     kp, kbar = permute_means(plan, k)
     vt = permute(plan, v, order=TILES_T)
+    if fused:
+        qbar = permute_means(plan, q, means_only=True)
+        kept = predict_mask(plan, qbar, kbar, sparsity_pct)
+        return sparse_attn_raster(plan, q, kp, vt, kept, sparsity_pct, scale=scale), kept
+    qp, qbar = permute_means(plan, q)
     kept = predict_mask(plan, qbar, kbar, sparsity_pct)
     op = sparse_attn(plan, qp, kp, vt, kept, sparsity_pct, scale=scale)
     return unpermute(plan, op), kept

@@ -219,7 +219,9 @@ rf_status rf_permute(const rf_plan* plan, const void* x, void* xp, int32_t B,
 /* rf_permute (RF_ROWS) fused with rf_block_means on the same tensor: the
  * permuted rows of x go to xp and the mean of each video block's valid
  * slots [RF2 Abstract insight (1)] to xbar, fp32 [B][H][nb][d], in one
- * pass over x.  Same arguments and errors as rf_permute. */
+ * pass over x.  xp may be null: then only the means are written (for a Q
+ * that rf_sparse_attn_raster reads in raster order).  Same arguments and
+ * errors as rf_permute. */
 rf_status rf_permute_means(const rf_plan* plan, const void* x, void* xp,
                            float* xbar, int32_t B, int32_t H, int32_t d,
                            rf_dtype dtype, hipStream_t stream);
@@ -284,6 +286,22 @@ rf_status rf_sparse_attn(const rf_plan* plan, const void* qp, const void* kp,
                          int32_t sparsity_pct, void* op, float* lse_or_null,
                          int32_t B, int32_t H, int32_t d, float scale,
                          rf_dtype dtype, hipStream_t stream);
+
+/* rf_sparse_attn with raster-order query and output: q [B][H][L][d] is the
+ * unpermuted query tensor (the slot of each query is found through the
+ * plan's tables, pad slots are never read), and o [B][H][L][d] receives the
+ * attention output of every token at its raster row, which is what
+ * rf_unpermute would make of rf_sparse_attn's output, bit for bit;
+ * lse_or_null, if given, is fp32 [B][H][L] in raster order.  kp and vt as
+ * for rf_sparse_attn (permuted, with the zero-pad precondition), kept_idx
+ * and sparsity_pct as for rf_sparse_attn.  Removes the permuted-Q write and
+ * the rf_unpermute pass from the path: rf_permute_means(Q, xp = null) gives
+ * the query means.  q and o must not overlap. */
+rf_status rf_sparse_attn_raster(const rf_plan* plan, const void* q, const void* kp,
+                                const void* vt, const int32_t* kept_idx,
+                                int32_t sparsity_pct, void* o, float* lse_or_null,
+                                int32_t B, int32_t H, int32_t d, float scale,
+                                rf_dtype dtype, hipStream_t stream);
 
 /* Attention-recall diagnostic [RF1 review, "What carries the argument":
  * the masked recall R', attention mass that survives a mask over the mass

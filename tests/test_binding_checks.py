@@ -185,3 +185,26 @@ def test_other_entry_points_refuse_mismatches(host):
         rf.permute_fp8(p, x, order=rf.TILES_T, scale=torch.zeros(B, H, z["n_tiles"]))
     with pytest.raises(ValueError):                       # recalls of different heads
         rf.arm_classify(torch.zeros(1, 2, 5), torch.zeros(1, 3, 5))
+
+
+def test_raster_attention_refuses_mismatches(host):
+    p = host
+    z = _z(p)
+    B, H, d = 1, 2, 64
+    q = torch.zeros(B, H, z["L"], d, dtype=torch.bfloat16)
+    qp, kp, vt = _ops(p)
+    kept = _kept(p, 20)
+    with pytest.raises(AssertionError, match="rf_sparse_attn_raster reached"):
+        rf.sparse_attn_raster(p, q, kp, vt, kept, 20)
+    for bad in (dict(q=qp), dict(kp=q), dict(kept=_kept(p, 50)),
+                dict(out=torch.zeros_like(qp))):
+        a = dict(q=q, kp=kp, vt=vt, kept=kept, out=None)
+        a.update(bad)
+        with pytest.raises(ValueError):
+            rf.sparse_attn_raster(p, a["q"], a["kp"], a["vt"], a["kept"], 20, out=a["out"])
+    # means only: no rows tensor is needed, and a wrong xbar is still refused
+    x = torch.zeros(B, H, z["L"], d, dtype=torch.bfloat16)
+    with pytest.raises(AssertionError, match="rf_permute_means reached"):
+        rf.permute_means(p, x, means_only=True)
+    with pytest.raises(ValueError):
+        rf.permute_means(p, x, means_only=True, xbar=torch.zeros(B, H, z["nb"] + 1, d))

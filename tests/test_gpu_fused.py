@@ -1,0 +1,100 @@
+"""The fused path (rf_permute_means without permuted rows for Q, then
+rf_sparse_attn_raster reading Q and writing O in raster order) gives the same
+bytes as the five-pass path (permute Q, attend on permuted rows, unpermute
+O), whose parity with the oracle test_gpu_parity.py checks; one small case is
+also checked against the oracle directly."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import parity
+from image_diffusion_dits_amd import configs, inputs, rf
+from oracle import rainfusion_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+CASES = [
+    ("ragged3d-text77", dict(T=3, H=13, W=21, wt=2, wh=8, ww=8, n_text=77, permute=1,
+                             sink=1), 2, 3, 128, torch.bfloat16, 70),
+    ("bs64-d64", dict(T=2, H=10, W=9, wt=1, wh=8, ww=8, n_text=0, permute=1, sink=1),
+     1, 2, 64, torch.bfloat16, 50),
+    ("raster-bs64-text10", dict(T=3, H=7, W=11, wt=1, wh=8, ww=8, n_text=10, permute=0,
+                                sink=1), 1, 2, 128, torch.bfloat16, 60),
+    ("bs128-d64", dict(T=2, H=9, W=17, wt=2, wh=8, ww=8, n_text=0, permute=1, sink=0),
+     1, 2, 64, torch.bfloat16, 40),
+    ("f32-d128-bs128-text5", dict(T=2, H=9, W=17, wt=2, wh=8, ww=8, n_text=5, permute=1,
+                                  sink=1), 1, 2, 128, torch.float32, 40),
+    ("f32-d64-bs64-raster", dict(T=2, H=5, W=30, wt=1, wh=8, ww=8, n_text=64, permute=0,
+                                 sink=1), 1, 2, 64, torch.float32, 75),
+    ("frames-smaller-than-window", dict(T=4, H=3, W=5, wt=2, wh=8, ww=8, n_text=3,
+                                        permute=1, sink=1), 1, 2, 128, torch.bfloat16, 50),
+]
+
+
+def _compare(lay, q, k, v, s):
+    plan = rf.Plan(lay)
+    z = plan.sizes
+    o_f, kept_f = rf.sparse_attention(q, k, v, plan, s, fused=True)
+    o_u, kept_u = rf.sparse_attention(q, k, v, plan, s, fused=False)
+    qbar_only = rf.permute_means(plan, q, means_only=True)
+    _, qbar = rf.permute_means(plan, q)
+    qp = rf.permute(plan, q)
+    kp, kbar = rf.permute_means(plan, k)
+    vt = rf.permute(plan, v, order=rf.TILES_T)
+    _, lse_slots = rf.sparse_attn(plan, qp, kp, vt, kept_u, s, lse=True)
+    o_r, lse_raster = rf.sparse_attn_raster(plan, q, kp, vt, kept_u, s, lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(qbar_only, qbar), "means-only pass"
+    assert torch.equal(kept_f, kept_u), "kept lists"
+    assert np.array_equal(parity.bits(o_f), parity.bits(o_u)), "fused output"
+    assert torch.equal(o_r, o_u)
+    _, tok_slot, _, _ = rf.layout_tables(lay)
+    want = lse_slots[:, :, torch.from_numpy(tok_slot.astype(np.int64)).cuda()]
+    assert torch.equal(lse_raster.view(torch.int32), want.view(torch.int32)), "raster LSE"
+    plan.close()
+    return o_f
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_fused_path_equals_five_pass_path(case):
+    name, lay, B, H, d, dt, s = case
+    say(f"[fused] {name} B={B} H={H} d={d} {dt} s={s}")
+    L = rf.layout_sizes(lay)["L"]
+    q, k, v = (inputs.random_tensor((B, H, L, d), sd, device="cuda", dtype=dt)
+               for sd in (31, 32, 33))
+    _compare(lay, q, k, v, s)
+
+
+def test_fused_path_720p_eight_heads():
+    cfg = configs.VIDEO720
+    say(f"[fused] {cfg.name} 8 heads s=80")
+    q, k, v = inputs.make_qkv(cfg, "cuda", H=8)
+    _compare(cfg.layout, q, k, v, 80)
+
+
+def test_fused_path_against_oracle():
+    """Raster output of the fused path equals the oracle's attention pulled
+    back to raster order (rows of the GPU's kept lists)."""
+    name, lay, B, H, d, dt, s = CASES[0]
+    say(f"[fused] oracle check on {name}")
+    L = rf.layout_sizes(lay)["L"]
+    q, k, v = (inputs.random_tensor((B, H, L, d), sd, device="cuda", dtype=dt)
+               for sd in (41, 42, 43))
+    plan = rf.Plan(lay)
+    o, kept = rf.sparse_attention(q, k, v, plan, s, fused=True)
+    torch.cuda.synchronize()
+    olay = parity.olayout(lay)
+    rows = rf.kept_rows(plan, kept, s)
+    qv, kv, vv = (parity.values(t) for t in (q, k, v))
+    qp, kp, vp = (orc.permute(t, olay) for t in (qv, kv, vv))
+    want = orc.unpermute(orc.sparse_attention(qp, kp, vp, rows, olay), olay)
+    err = np.abs(parity.values(o) - want)
+    assert err.max() <= parity.TOL["bf16"][0] and err.mean() <= parity.TOL["bf16"][1]
+    plan.close()

@@ -6,6 +6,7 @@ sizes, both head dims and both precisions; the five synthetic workloads run
 at full size with all heads checked for the permutation, means and masks and
 sampled query tiles for attention (all tiles of two heads).
 """
+import os
 import sys
 
 import numpy as np
@@ -36,10 +37,12 @@ def run_gpu(plan, q, k, v, s, logits=False):
 
 
 def check_case(lay_dict, q, k, v, s, dtype, full_heads=None, sample_tiles=None,
-               seed=0, gpu=None):
+               seed=0, gpu=None, check_lse=True, record=None):
     """Run the GPU path on q, k, v (device tensors) and check it against the
     oracle.  full_heads: heads whose every query tile is checked for
-    attention (None = all); other heads get `sample_tiles` random tiles."""
+    attention (None = all); other heads get `sample_tiles` random tiles.
+    check_lse=False skips the oracle's log-sum-exp (checked on other cases).
+    record: optional dict that receives the point's statistics."""
     lay = parity.olayout(lay_dict)
     z = orc.sizes(lay)
     plan = rf.Plan(lay_dict)
@@ -62,7 +65,7 @@ def check_case(lay_dict, q, k, v, s, dtype, full_heads=None, sample_tiles=None,
     op = parity.values(g["op"][:, :, :Lp])
     for name in ("qp", "kp", "op"):        # whole-tile pad rows after Lp
         assert torch.all(g[name][:, :, Lp:] == 0), name
-    lse = parity.values(g["lse"]) if "lse" in g else None
+    lse = parity.values(g["lse"]) if ("lse" in g and check_lse) else None
     if lse is not None:
         assert np.all(np.isneginf(lse[:, :, Lp:])), "LSE of whole-tile pad rows"
     dense = g["dense"].cpu().numpy() if "dense" in g else None
@@ -114,6 +117,10 @@ def check_case(lay_dict, q, k, v, s, dtype, full_heads=None, sample_tiles=None,
             stats["max_abs"] = max(stats["max_abs"], mx)
             stats["mean_abs"].append(mn)
     plan.close()
+    if record is not None:
+        record.update(swaps=stats["swaps"], max_abs=stats["max_abs"],
+                      mean_abs=float(np.mean(stats["mean_abs"])),
+                      lse_max_abs=max(stats.get("lse", [float("nan")])))
     say(f"  swaps={stats['swaps']} max_abs={stats['max_abs']:.3e} "
         f"mean_abs={np.mean(stats['mean_abs']):.3e} "
         f"lse_max_abs={max(stats.get('lse', [float('nan')])):.3e}")
@@ -198,14 +205,58 @@ def test_video_long_text_workload():
                full_heads={0, cfg.H // 2}, sample_tiles=16)
 
 
+def _sweep_record(cfg, s, q, k, v, rec):
+    """One JSON line per sweep point (input sha256s, swaps, errors, host),
+    appended to $RF_PARITY_RECORD when that is set."""
+    path = os.environ.get("RF_PARITY_RECORD")
+    if not path:
+        return
+    import json
+    line = dict(workload=cfg.name, sparsity_pct=s, permute=cfg.permute, heads=q.shape[1],
+                inputs_sha256={n: inputs.sha256(t) for n, t in (("q", q), ("k", k),
+                                                                 ("v", v))},
+                nproc=os.cpu_count(), **rec)
+    try:
+        with open("/proc/cpuinfo") as f:
+            line["cpu_model"] = next((l.split(":", 1)[1].strip() for l in f
+                                      if l.startswith("model name")), "")
+    except OSError:
+        pass
+    with open(path, "a") as f:
+        f.write(json.dumps(line) + "\n")
+
+
 @pytest.mark.parametrize("permute", [1, 0])
 def test_sweep_workload(permute):
+    """Every sweep point at the full 40 heads, in window and raster order:
+    permutation, means and masks on every head, attention on 3 sampled query
+    tiles of every head (the full acceptance is test_sweep_full_acceptance)."""
     cfg = configs.SWEEP if permute else configs.SWEEP_RASTER
-    q, k, v = inputs.make_qkv(cfg, "cuda", H=4)
+    q, k, v = inputs.make_qkv(cfg, "cuda")
     for s in cfg.sparsity:
-        say(f"[workload] {cfg.name} s={s} (4 heads, 12 tiles each)")
+        say(f"[workload] {cfg.name} s={s} (40 heads; attention: 3 tiles each)")
+        rec = {}
         check_case(cfg.layout, q, k, v, s, "bf16", full_heads=set(),
-                   sample_tiles=12, seed=s)
+                   sample_tiles=3, seed=s, check_lse=False, record=rec)
+        _sweep_record(cfg, s, q, k, v, dict(rec, check="sampled-3"))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("permute", [1, 0])
+def test_sweep_full_acceptance(permute):
+    """The sweep's acceptance at the full 40 heads: masks on every head,
+    attention on every query tile of heads 0 and 20 and on 16 sampled tiles
+    of every other head, at every sparsity, in window and raster order.  The
+    log-sum-exp is left to the other workload tests."""
+    cfg = configs.SWEEP if permute else configs.SWEEP_RASTER
+    q, k, v = inputs.make_qkv(cfg, "cuda")
+    for s in cfg.sparsity:
+        say(f"[acceptance] {cfg.name} s={s} (40 heads; attention: heads 0, 20 in full, "
+            f"16 tiles elsewhere)")
+        rec = {}
+        check_case(cfg.layout, q, k, v, s, "bf16", full_heads={0, cfg.H // 2},
+                   sample_tiles=16, seed=100 + s, check_lse=False, record=rec)
+        _sweep_record(cfg, s, q, k, v, dict(rec, check="full-heads-0-20+16"))
 
 
 @pytest.mark.parametrize("T,d", [(16, 128), (17, 64), (17, 128), (64, 64)],
@@ -287,6 +338,15 @@ def test_gpu_argument_errors():
                                  ctypes.byref(nt)) == 0
     assert (n.value, n_p.value, nb.value, bs.value, ns.value, nt.value) == \
         (z["N"], z["Np"], z["nb"], z["bs"], z["n_sink"], z["n_text_tiles"])
+    # rf_keep_count on the plan agrees with rf_layout_keep on its layout.
+    for cfg in (configs.TINY, configs.VIDEO_LONG, configs.SWEEP_RASTER):
+        p2 = rf.Plan(cfg.layout)
+        for s in (0, 50, 80, 95, 99):
+            want = rf.keep_count(cfg.layout, s)
+            assert p2.keep_count(s) == (want["k_eff"], want["nnz_per_head"])
+        with pytest.raises(rf.RfError):
+            p2.keep_count(100)
+        p2.close()
     x = torch.zeros(1, 2, z["L"], 64, device="cuda")
     with pytest.raises(rf.RfError) as e:
         rf.permute(plan, x[..., :48].contiguous())       # d = 48
@@ -317,4 +377,67 @@ def test_gpu_argument_errors():
                           kept.data_ptr(), 50, xp.data_ptr(), xp.data_ptr() + 2, 1, 2,
                           64, 0.125, rf.F32, None)
     assert st == rf.ERR_INVALID_ARG and b"lse" in L.rf_last_error()
+    plan.close()
+
+
+PAD_LAYOUTS = [
+    # partial tiles in t, h and w, text with a partial tile; bs = 128 and 64
+    ("bs128-partial", dict(T=3, H=13, W=21, wt=2, wh=8, ww=8, n_text=77, permute=1,
+                           sink=1), 128, 60),
+    ("bs64-partial", dict(T=3, H=13, W=21, wt=1, wh=8, ww=8, n_text=77, permute=1,
+                          sink=1), 64, 60),
+    ("bs128-raster-tail", dict(T=3, H=7, W=11, wt=2, wh=8, ww=8, n_text=0, permute=0,
+                               sink=1), 128, 50),
+]
+
+
+@pytest.mark.parametrize("case", PAD_LAYOUTS, ids=[c[0] for c in PAD_LAYOUTS])
+def test_permute_writes_zero_pads_and_attention_matches_oracle(case):
+    """rf_sparse_attn requires zero pad rows in kp and zero pad columns in
+    vt, which rf_permute writes: output buffers pre-filled with finite
+    garbage (3.0) hold exact zeros at every pad slot afterwards, and both
+    the 128-slot and the 64-slot kernels then match the oracle.  The 64-slot
+    kernel masks pad keys itself, so garbage written into the pads after the
+    permutation leaves its result unchanged (documented behaviour; the
+    128-slot kernels' result is unspecified then and is not tested)."""
+    name, lay, bs, s = case
+    say(f"[pads] {name} s={s}")
+    plan = rf.Plan(lay)
+    z = plan.sizes
+    assert z["bs"] == bs
+    olay = parity.olayout(lay)
+    valid = orc.slot_valid(olay)
+    valid_lt = np.concatenate([valid, np.zeros(z["Lt"] - z["Lp"], bool)])
+    assert not valid_lt.all(), "the layout must have pad slots"
+    B, H, d = 1, 2, 128
+    q, k, v = (_iid((B, H, z["L"], d), sd, torch.bfloat16) for sd in (51, 52, 53))
+    qp = rf.permute(plan, q)
+    kp = torch.full((B, H, z["Lt"], d), 3.0, dtype=torch.bfloat16, device="cuda")
+    vt = torch.full((B, H, z["n_tiles"], d, bs), 3.0, dtype=torch.bfloat16, device="cuda")
+    rf.permute(plan, k, out=kp)
+    rf.permute(plan, v, order=rf.TILES_T, out=vt)
+    qbar, kbar = rf.block_means(plan, qp, kp)
+    kept = rf.predict_mask(plan, qbar, kbar, s)
+    op = rf.sparse_attn(plan, qp, kp, vt, kept, s)
+    torch.cuda.synchronize()
+    pad = torch.from_numpy(~valid_lt).cuda()
+    assert torch.all(kp[:, :, pad] == 0), "pad rows of kp"
+    vt_slots = vt.permute(0, 1, 2, 4, 3).reshape(B, H, z["Lt"], d)
+    assert torch.all(vt_slots[:, :, pad] == 0), "pad columns of vt"
+    rows = rf.kept_rows(plan, kept, s)
+    Lp = z["Lp"]
+    for h in range(H):
+        sl = (slice(0, 1), slice(h, h + 1))
+        want = orc.sparse_attention(parity.values(qp[sl][..., :Lp, :]),
+                                    parity.values(kp[sl][..., :Lp, :]),
+                                    orc.permute(parity.values(v[sl]), olay),
+                                    [[rows[0][h]]], olay)
+        parity.check_attention(parity.values(op[0, h, :Lp]), want[0, 0], valid, "bf16")
+    if bs == 64:
+        kp[:, :, pad] = 3.0
+        vt_slots[:, :, pad] = 3.0
+        vt2 = vt_slots.reshape(B, H, z["n_tiles"], bs, d).permute(0, 1, 2, 4, 3).contiguous()
+        op2 = rf.sparse_attn(plan, qp, kp, vt2, kept, s)
+        torch.cuda.synchronize()
+        assert torch.equal(op2, op), "64-slot kernel with garbage pads"
     plan.close()

@@ -347,6 +347,12 @@ def test_pattern_argument_errors():
     with pytest.raises(rf.RfError):
         rf.arm_recall(plan, q, q, True, 2, 5, 1)                # unknown pattern
     rows = torch.zeros((1, 2, z["n_tiles"], z["n_tiles"] + 1), dtype=torch.int32, device="cuda")
-    with pytest.raises(rf.RfError):
-        rf.sparse_attn_rows(plan, q, q, q, rows)                # width > n_tiles
+    vt = torch.zeros((1, 2, z["n_tiles"], 64, z["bs"]), device="cuda")
+    with pytest.raises(ValueError):                         # the binding refuses first
+        rf.sparse_attn_rows(plan, q, q, vt, rows)
+    L = rf.lib()                                            # and so does the library
+    P = lambda t: t.data_ptr()
+    st = L.rf_sparse_attn_rows(plan.handle, P(q), P(q), P(vt), P(rows), z["n_tiles"] + 1,
+                               P(q), None, 1, 2, 64, 0.125, rf.F32, None)
+    assert st == rf.ERR_INVALID_ARG and b"row_width" in L.rf_last_error()
     plan.close()
