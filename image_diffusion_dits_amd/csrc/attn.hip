@@ -420,7 +420,11 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
   const __attribute__((address_space(4))) int32_t* row =
       (const __attribute__((address_space(4))) int32_t*)(kept + bh * nnz + rr.offset);
   const int32_t row_len = rr.len;
-  const int32_t n_grp = (row_len + 1) / 2;   // tiles per group; group 1 may end on a masked one
+  // Phase pairs of the walk: group 0 takes the even entries, group 1 the
+  // odd ones, so on an odd row group 1 has one step fewer; it still takes
+  // part in every barrier but does no work in its missing step.
+  const int32_t n_grp = (row_len + 1) / 2;
+  const int32_t n_own = (row_len + 1 - grp) / 2;
   // Kept tile of this group's tile i, or -1: entries past the end and ids out
   // of range are walked as fully masked tiles (whose copies read tile 0).
   auto tile_of = [&](int32_t i) -> int32_t {
@@ -487,7 +491,7 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
     asm volatile("" : "+v"(vlane), "+v"(vx), "+v"(klane), "+v"(kx));
     const char* const vs = reinterpret_cast<const char*>(vsg) + vlane;
     const char* const kq = reinterpret_cast<const char*>(ks) + klane;
-    if (i >= 1) {
+    if (i >= 1 && i - 1 < n_own) {
       // O^T[db] += V^T[db rows, keys] P^T(i-1); MFMA (kb, h) takes keys
       // kb*32 + 16h + 8g .. +8 in lane group g.
 #pragma unroll
@@ -506,7 +510,7 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
     }
     // P(i-1) dies with the PV above before the scores of tile i are born.
     __builtin_amdgcn_sched_barrier(0);
-    if (i < n_grp) {
+    if (i < n_own) {
       // S^T blocks: s[kb] covers keys kb*32 .. +32 x the wave's 32 queries.
       // MFMA row x of block kb is fed K row kb*32 + sigma(x), so
       // accumulator register r = 4a + b of lane group g holds key
@@ -541,9 +545,9 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
   // VALU phase of tile i: the copies of K(i+1) and V^T(i) (their buffers
   // were last read in the MFMA phase just finished) and softmax(i).
   auto valu_phase = [&](int32_t i) {
-    if (i < 0 || i >= n_grp) return;
+    if (i < 0 || i >= n_own) return;
     const int32_t kt = kt_cur;
-    const bool next_k = i + 1 < n_grp;
+    const bool next_k = i + 1 < n_own;
     const TileCopy<C::kGroupWaves> ck(kh + int64_t(max(next_k ? kt_nxt : 0, 0)) *
                                           C::kTileBytes, C::kTileBytes, ks, koff, qw);
     const TileCopy<C::kGroupWaves> cv(vh + int64_t(max(kt, 0)) * C::kTileBytes, C::kTileBytes,
@@ -680,7 +684,7 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
     bits_cur = bits_n;
   };
 
-  if (n_grp > 0) {
+  if (n_own > 0) {
     poison_tile<C::kCopies, C::kGroupWaves>(ks, qw, lane);
     copy_k(kt_cur);
   }
@@ -688,7 +692,7 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
   // still pending at the loop entry would make the compiler wait on all LDS
   // reads at once (lgkmcnt(0)) at the start of each MFMA phase.
   asm volatile("" ::"s"(kt_nxt), "s"(bits_cur.x), "s"(bits_cur.y), "s"(bits_cur.z),
-               "s"(bits_cur.w), "s"(scale_log2), "s"(n_grp), "s"(row_len));
+               "s"(bits_cur.w), "s"(scale_log2), "s"(n_grp), "s"(n_own), "s"(row_len));
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __builtin_amdgcn_s_barrier();
   // Phase pairs: group 0 runs MFMA(i) then VALU(i); group 1 runs VALU(i-1)

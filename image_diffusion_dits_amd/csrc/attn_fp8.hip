@@ -107,7 +107,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
   const __attribute__((address_space(4))) int32_t* row =
       (const __attribute__((address_space(4))) int32_t*)(kept + bh * nnz + rr.offset);
   const int32_t row_len = rr.len;
+  // Phase pairs of the walk; on an odd row group 1 has one step fewer and
+  // does no work in the missing one (it still takes part in the barriers).
   const int32_t n_grp = (row_len + 1) / 2;
+  const int32_t n_own = (row_len + 1 - grp) / 2;
   auto tile_of = [&](int32_t i) -> int32_t {
     const int32_t j = 2 * i + grp;
     const int32_t kt = row[max(min(j, row_len - 1), 0)];
@@ -212,7 +215,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
   auto mfma_phase = [&](int32_t i) {
     int lrow = li * kRowBytes, x0 = ((2 * g) ^ rswz) * 16, x1 = ((2 * g + 1) ^ rswz) * 16;
     asm volatile("" : "+v"(lrow), "+v"(x0), "+v"(x1));
-    if (i >= 1) {
+    if (i >= 1 && i - 1 < n_own) {
       // O^T[db] += V^T[db rows, keys 64s .. +64] P^T(i-1), k-steps s = 0, 1.
       const uint8_t* const vs = vslot + ((i - 1) & 1) * kTileBytes + lrow;
 #pragma unroll
@@ -225,7 +228,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
       lsum = mma(row_sum_operand(1), pb[1], lsum);
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (i < n_grp) {
+    if (i < n_own) {
       const uint8_t* const ks = kslot + (i & 1) * kTileBytes + lrow;
 #pragma unroll
       for (int kb = 0; kb < BS / 32; ++kb) {
@@ -240,7 +243,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
       // this phase's LDS reads: their issue stalls fall in the wait at the
       // barrier, and the group's VALU phase waits for them at its end.
       __builtin_amdgcn_sched_barrier(0);
-      if (i + 1 < n_grp) {
+      if (i + 1 < n_own) {
         poison_tile<kCopies, kGroupWaves>(kslot + ((i + 1) & 1) * kTileBytes, qw, lane);
         copy_k(kt_nxt, (i + 1) & 1);
       }
@@ -250,7 +253,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
   };
 
   auto valu_phase = [&](int32_t i) {
-    if (i < 0 || i >= n_grp) return;
+    if (i < 0 || i >= n_own) return;
     const int32_t kt = kt_cur;
     // The next step's scalars (in flight during the softmax).
     const int32_t kt_n2 = tile_of(i + 2);
@@ -334,14 +337,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
     ks_cur = ks_n;
   };
 
-  if (n_grp > 0) {
+  if (n_own > 0) {
     poison_tile<kCopies, kGroupWaves>(kslot, qw, lane);
     copy_k(kt_cur, 0);
   }
   // Every scalar the loop reads is resident before it starts (a scalar load
   // pending at the loop entry would coarsen the LDS waits of every phase).
   asm volatile("" ::"s"(kt_nxt), "s"(bits_cur.x), "s"(bits_cur.y), "s"(bits_cur.z),
-               "s"(bits_cur.w), "s"(ks_cur), "s"(scale_log2), "s"(c_q), "s"(n_grp),
+               "s"(bits_cur.w), "s"(ks_cur), "s"(scale_log2), "s"(c_q), "s"(n_grp), "s"(n_own),
                "s"(row_len));
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __builtin_amdgcn_s_barrier();
