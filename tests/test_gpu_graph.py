@@ -1,9 +1,10 @@
 """The path on a non-default stream and inside a captured HIP graph.
 
 Every hot entry point only enqueues kernels on the caller's stream, so the
-whole path (permute and pool Q and K, permute V, predict, attend, unpermute;
-and its FP8 form) runs on a side stream and can be captured once and
-replayed.  The replays run with eager launches of the same path and host
+whole path runs on a side stream and can be captured once and replayed: the
+fused path (means of Q, permute and pool K, permute V, predict, attend with
+raster-order Q and O), the five-pass path (permute Q too, attend, unpermute)
+and the FP8 form.  The replays run with eager launches of the same path and host
 synchronisations between them, and each replay's output must equal the eager
 result bit for bit.
 """
@@ -21,7 +22,12 @@ def say(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-CASES = [("bf16", rf.sparse_attention), ("fp8", rf.sparse_attention_fp8)]
+def _five_pass(q, k, v, plan, s):
+    return rf.sparse_attention(q, k, v, plan, s, fused=False)
+
+
+CASES = [("bf16-fused", rf.sparse_attention), ("bf16-five-pass", _five_pass),
+         ("fp8", rf.sparse_attention_fp8)]
 
 
 @pytest.mark.parametrize("name,path", CASES, ids=[c[0] for c in CASES])
