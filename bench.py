@@ -544,6 +544,15 @@ def measure(a, cfg, s, q, k, v):
     attn_median = statistics.median(e[j_attn].elapsed_time(e[j_attn + 1]) for e in evs)
 
     pairs = kc["nnz_per_head"] * B * H
+    # Valid work: the (query, key) pairs of kept tiles whose slots both hold a
+    # token (the executed count includes the pad slots of partial tiles).
+    _, _, tile_count, _ = rf.layout_tables(cfg.layout)
+    cnt = torch.from_numpy(tile_count.astype("int64")).to(dev)
+    kept_l = kept.view(B * H, -1).long()
+    n_tiles = z["n_tiles"]
+    rows_t = torch.cat([torch.arange(z["nb"], device=dev).repeat_interleave(kc["row_len_video"]),
+                        torch.arange(z["nb"], n_tiles, device=dev).repeat_interleave(kc["row_len_text"])])
+    valid_pairs = int((cnt[rows_t][None, :] * cnt[kept_l]).sum())
     exec_flop = 4.0 * d * bs * bs * pairs
     L = z["L"]
     dense_flop = 4.0 * B * H * L * L * d
@@ -590,6 +599,8 @@ def measure(a, cfg, s, q, k, v):
         "attn_ms": round(stage_ms["sparse_attn"], 4),
         "attn_ms_median": round(attn_median, 4),
         "attn_exec_tflops": round(attn_tflops, 2),
+        "attn_valid_tflops": round(4.0 * d * valid_pairs / attn_s / 1e12, 2),
+        "valid_pair_share": round(valid_pairs / (pairs * bs * bs), 4),
         "attn_dense_equiv_tflops": round(dense_flop / attn_s / 1e12, 2),
         "mfma_util": round(attn_tflops / peak, 4),
         "exec_tflop_per_call": round(exec_flop / 1e12, 4),
