@@ -22,8 +22,12 @@ import argparse
 import hashlib
 import json
 import os
+import re
+import shutil
 import statistics
+import subprocess
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -390,6 +394,51 @@ def main():
     return 0
 
 
+class ClockSampler:
+    """Reads the GPU's shader clock (SCLK) with rocm-smi, over and over, while
+    the timed steps run, so that each record says at what clock its rate was
+    reached.  Under sustained matrix-core load the clock sits well below the
+    2.4 GHz the published peaks assume.  Gives None where rocm-smi is absent
+    or no reading finished inside the timed region."""
+
+    PATTERN = re.compile(r"sclk clock level: \S+ \((\d+)Mhz\)")
+
+    def __init__(self):
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = None
+
+    def __enter__(self):
+        if shutil.which("rocm-smi") is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True,
+                                   text=True, timeout=5)
+            except (OSError, subprocess.SubprocessError):
+                return
+            found = self.PATTERN.findall(r.stdout)
+            if found and not self._stop.is_set():
+                # The busiest GPU the tool lists (a box shows only its own).
+                self.samples.append(max(int(x) for x in found))
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join(timeout=10)
+        return False
+
+    def record(self):
+        if not self.samples:
+            return None
+        return {"median": statistics.median(self.samples), "min": min(self.samples),
+                "max": max(self.samples), "samples": len(self.samples)}
+
+
 def host_info():
     """Host facts recorded beside each measurement."""
     model = ""
@@ -537,6 +586,16 @@ def measure(a, cfg, s, q, k, v):
     for i in range(a.steps):
         step(evs[i])
     torch.cuda.synchronize()
+
+    # Region 3, not timed: the same steps for about half a second while the
+    # shader clock is sampled (the sampler's subprocesses would otherwise
+    # compete with the launches of a short step).
+    with ClockSampler() as clock:
+        t_end = time.perf_counter() + 0.5
+        while time.perf_counter() < t_end:
+            for _ in range(max(1, min(a.steps, 50))):
+                step()
+            torch.cuda.synchronize()
     stage_ms = {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / a.steps
                 for j, name in enumerate(stages)}
     ev_step_ms = sum(e[0].elapsed_time(e[n_ev - 1]) for e in evs) / a.steps
@@ -621,6 +680,9 @@ def measure(a, cfg, s, q, k, v):
             "permute_v": round(perm_bytes / (stage_ms["permute_v"] / 1e3) / 1e9, 1),
             "unpermute": round(unperm_bytes / (stage_ms["unpermute"] / 1e3) / 1e9, 1),
         }),
+        # Shader clock while the same steps run (rocm-smi samples, region 3);
+        # the peaks above are quoted at 2.4 GHz.
+        "sclk_mhz": clock.record(),
         "roofline": {
             "kernel": kernel,
             "bound": "mfma",

@@ -212,7 +212,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
     return g ? w1 : w0;
   };
 
+  // The wave in its MFMA phase takes issue priority over the softmax wave on
+  // its SIMD.  Otherwise the older wave wins each issue cycle whatever it
+  // runs: in the phase where group 1 issues MFMAs beside group 0's softmax,
+  // its MFMAs waited for issue slots and that phase took about 700 cycles
+  // more than the other (per step, 720p video).
   auto mfma_phase = [&](int32_t i) {
+    __builtin_amdgcn_s_setprio(3);
     int lrow = li * kRowBytes, x0 = ((2 * g) ^ rswz) * 16, x1 = ((2 * g + 1) ^ rswz) * 16;
     asm volatile("" : "+v"(lrow), "+v"(x0), "+v"(x1));
     if (i >= 1 && i - 1 < n_own) {
@@ -250,6 +256,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
       poison_tile<kCopies, kGroupWaves>(vslot + (i & 1) * kTileBytes, qw, lane);
       copy_v(kt_cur, i & 1);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   auto valu_phase = [&](int32_t i) {
