@@ -88,6 +88,11 @@ def parse():
                     help="instead of the step benchmark, time the v1 head-pattern "
                          "path on the 720p workload: ARM recall and decision, "
                          "pattern rows, and block-sparse attention on them")
+    ap.add_argument("--reference-gemm", action="store_true",
+                    help="instead of the step benchmark, time the vendor library's "
+                         "dense bf16 GEMM (torch.matmul, 8192^3) on the same GPU, "
+                         "with the shader clock it holds: the rate a dense bf16 "
+                         "matrix-core kernel reaches on this part")
     return ap.parse_args()
 
 
@@ -264,6 +269,45 @@ def recall_study(n_sample):
     return 0
 
 
+def reference_gemm(n=8192, calls=50):
+    """Rate of the vendor library's dense bf16 GEMM (torch.matmul, which
+    dispatches to hipBLASLt) on an n x n x n product, timed with HIP events,
+    and the shader clock held meanwhile.  Context for the attention's rate:
+    this is what a tuned dense matrix-core kernel reaches here, against the
+    same 2.5 PFLOP/s peak quoted at 2.4 GHz."""
+    import torch
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    g = torch.Generator(device=dev).manual_seed(0)
+    x = torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=g)
+    y = torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=g)
+    out = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(10):
+        torch.matmul(x, y, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(calls):
+        torch.matmul(x, y, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / calls
+    with ClockSampler() as clock:
+        t_end = time.perf_counter() + 0.5
+        while time.perf_counter() < t_end:
+            for _ in range(10):
+                torch.matmul(x, y, out=out)
+            torch.cuda.synchronize()
+    tflops = 2.0 * n ** 3 / (ms / 1e3) / 1e12
+    print(json.dumps({"metric": "dense bf16 GEMM TFLOP/s (torch.matmul, vendor library)",
+                      "value": round(tflops, 2), "unit": "TFLOP/s", "n": n,
+                      "ms_per_call": round(ms, 4), "calls": calls,
+                      "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+                      "peak": PEAK_BF16_TFLOPS, "sclk_mhz": clock.record()}), flush=True)
+    return 0
+
+
 def source_hash(kernel):
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kernel]:
@@ -368,6 +412,8 @@ def main():
                               a.sparsity if a.sparsity is not None else 80)
     if a.patterns:
         return pattern_study()
+    if a.reference_gemm:
+        return reference_gemm()
     if a.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported "
               "(every step is independent per head; the multi-GPU layout is "
@@ -398,8 +444,8 @@ class ClockSampler:
     """Reads the GPU's shader clock (SCLK) with rocm-smi, over and over, while
     the timed steps run, so that each record says at what clock its rate was
     reached.  Under sustained matrix-core load the clock sits well below the
-    2.4 GHz the published peaks assume.  Gives None where rocm-smi is absent
-    or no reading finished inside the timed region."""
+    2.4 GHz the published peaks assume.  Gives None where rocm-smi is absent,
+    under a profiler, or when no reading finished in time."""
 
     PATTERN = re.compile(r"sclk clock level: \S+ \((\d+)Mhz\)")
 
@@ -408,8 +454,15 @@ class ClockSampler:
         self._stop = threading.Event()
         self._thread = None
 
+    @staticmethod
+    def profiler_attached():
+        """True under rocprofv3, whose preloaded library would initialise the
+        GPU in the sampler's child processes too."""
+        return ("rocprof" in os.environ.get("LD_PRELOAD", "")
+                or any(k.startswith("ROCPROF") for k in os.environ))
+
     def __enter__(self):
-        if shutil.which("rocm-smi") is not None:
+        if shutil.which("rocm-smi") is not None and not self.profiler_attached():
             self._thread = threading.Thread(target=self._run, daemon=True)
             self._thread.start()
         return self

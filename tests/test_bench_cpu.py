@@ -81,3 +81,13 @@ def test_traffic_record_is_keyed_to_the_kernel_source(tmp_path, monkeypatch):
     assert bench.stored_traffic(kernel, "video720-21x45x80") is None    # kernel changed since
     f.write_text("not json")
     assert bench.stored_traffic(kernel, "video720-21x45x80") is None
+
+
+def test_clock_sampler_stays_off_under_a_profiler(monkeypatch):
+    calls = []
+    monkeypatch.setattr(bench.shutil, "which", lambda name: "/usr/bin/" + name)
+    monkeypatch.setattr(bench.subprocess, "run", lambda *a, **k: calls.append(a))
+    monkeypatch.setenv("ROCPROF_KERNEL_TRACE", "1")
+    with bench.ClockSampler() as clock:
+        time.sleep(0.01)
+    assert clock.record() is None and calls == []
