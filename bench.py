@@ -293,8 +293,9 @@ def reference_gemm(n=8192, calls=50):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / calls
-    with ClockSampler() as clock:
-        t_end = time.perf_counter() + 0.5
+    clock = ClockSampler()
+    with clock:
+        t_end = time.perf_counter() + (0.5 if clock.available() else 0.0)
         while time.perf_counter() < t_end:
             for _ in range(10):
                 torch.matmul(x, y, out=out)
@@ -461,8 +462,11 @@ class ClockSampler:
         return ("rocprof" in os.environ.get("LD_PRELOAD", "")
                 or any(k.startswith("ROCPROF") for k in os.environ))
 
+    def available(self):
+        return shutil.which("rocm-smi") is not None and not self.profiler_attached()
+
     def __enter__(self):
-        if shutil.which("rocm-smi") is not None and not self.profiler_attached():
+        if self.available():
             self._thread = threading.Thread(target=self._run, daemon=True)
             self._thread.start()
         return self
@@ -643,12 +647,14 @@ def measure(a, cfg, s, q, k, v):
     # Region 3, not timed: the same steps for about half a second while the
     # shader clock is sampled (the sampler's subprocesses would otherwise
     # compete with the launches of a short step).
-    with ClockSampler() as clock:
-        t_end = time.perf_counter() + 0.5
-        while time.perf_counter() < t_end:
-            for _ in range(max(1, min(a.steps, 50))):
-                step()
-            torch.cuda.synchronize()
+    clock = ClockSampler()
+    if clock.available():
+        with clock:
+            t_end = time.perf_counter() + 0.5
+            while time.perf_counter() < t_end:
+                for _ in range(max(1, min(a.steps, 50))):
+                    step()
+                torch.cuda.synchronize()
     stage_ms = {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / a.steps
                 for j, name in enumerate(stages)}
     ev_step_ms = sum(e[0].elapsed_time(e[n_ev - 1]) for e in evs) / a.steps
