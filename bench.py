@@ -88,6 +88,10 @@ def parse():
                     help="instead of the step benchmark, time the v1 head-pattern "
                          "path on the 720p workload: ARM recall and decision, "
                          "pattern rows, and block-sparse attention on them")
+    ap.add_argument("--heads", type=int, default=None,
+                    help="time the workload on this many heads instead of all: one "
+                         "GPU's share when the heads are split across GPUs (the "
+                         "720p workload's 40 heads over 8 GPUs is --heads 5)")
     ap.add_argument("--reference-gemm", action="store_true",
                     help="instead of the step benchmark, time the vendor library's "
                          "dense bf16 GEMM (torch.matmul, 8192^3) on the same GPU, "
@@ -432,7 +436,10 @@ def main():
     s = a.sparsity if a.sparsity is not None else (80 if a.config == 5 else cfg.sparsity[0])
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    q, k, v = inputs.make_qkv(cfg, dev)
+    if a.heads is not None and not 1 <= a.heads <= cfg.H:
+        print(f"--heads must be in 1..{cfg.H} for {cfg.name}", file=sys.stderr)
+        return 2
+    q, k, v = inputs.make_qkv(cfg, dev, H=a.heads)
     rec, exec_flop = measure(a, cfg, s, q, k, v)
     if not a.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(cfg, q, k, v, s, a.cpu_tiles, exec_flop, a.fp8,
