@@ -7,7 +7,9 @@ One step is one pass of the whole path over one attention call of the
 workload: permute K and V (3D windows), pool the block means of Q and K,
 predict the mask, block-sparse attention reading Q and writing O in raster
 order (the fused path; --unfused permutes Q and unpermutes O in passes of
-their own, as the FP8 path does).  Inputs are synthetic (seeded) and
+their own).  With --fp8 the permutations quantize Q, K and V to e4m3 and
+the attention writes O in raster order (--unfused: slot order, then an
+unpermute pass).  Inputs are synthetic (seeded) and
 resident in HBM before timing starts; every output buffer is allocated
 beforehand, so the timed region only launches kernels.
 
@@ -63,7 +65,8 @@ def parse():
                     help="one JSON line per workload point (all configurations, the "
                          "720p sparsity sweep in window and raster order)")
     ap.add_argument("--unfused", action="store_true",
-                    help="permute Q and unpermute O in passes of their own")
+                    help="attend in slot order and unpermute O in a pass of its own "
+                         "(bf16: and permute Q in a pass of its own)")
     ap.add_argument("--cpu-tiles", type=int, default=660,
                     help="query tiles in the oracle's attention sample")
     ap.add_argument("--cpu-heads", type=int, default=2,
@@ -584,9 +587,11 @@ def measure(a, cfg, s, q, k, v):
         ks = torch.empty_like(qs)
         vs = torch.empty(B, H, d, dtype=torch.float32, device=dev)
 
-    fused = not (a.fp8 or a.unfused)
+    fused = not a.unfused
     if a.fp8:
-        stages = ["permute_fp8_qk", "permute_fp8_v", "predict_mask", "sparse_attn", "unpermute"]
+        stages = ["permute_fp8_qk", "permute_fp8_v", "predict_mask", "sparse_attn"]
+        if not fused:
+            stages.append("unpermute")
     elif fused:
         stages = ["means_q_permute_means_k", "permute_v", "predict_mask", "sparse_attn"]
     else:
@@ -619,7 +624,9 @@ def measure(a, cfg, s, q, k, v):
         mark()
         rf.predict_mask(plan, qbar, kbar, s, kept=kept)
         mark()
-        if a.fp8:
+        if a.fp8 and fused:
+            rf.sparse_attn_fp8_raster(plan, q8, qs, k8, ks, v8, vs, kept, s, out=o)
+        elif a.fp8:
             rf.sparse_attn_fp8(plan, q8, qs, k8, ks, v8, vs, kept, s, out=op)
         elif fused:
             rf.sparse_attn_raster(plan, q, kp, vt, kept, s, out=o)
@@ -714,7 +721,8 @@ def measure(a, cfg, s, q, k, v):
         "dtype": "fp8" if a.fp8 else cfg.dtype,
         "data": "synthetic",
         "config": {
-            "workload": workload, "path": ("fp8" if a.fp8 else "fused" if fused else "five-pass"),
+            "workload": workload,
+            "path": ("fp8-" if a.fp8 else "") + ("fused" if fused else "five-pass"),
             "batch": B, "heads": H, "head_dim": d,
             "tokens": z["N"], "text_tokens": z["L"] - z["N"],
             "padded_slots": z["Lp"], "block": bs, "blocks": z["nb"],
@@ -733,11 +741,12 @@ def measure(a, cfg, s, q, k, v):
         "stages_ms": {n: round(x, 4) for n, x in stage_ms.items()},
         "event_ms_per_step": round(ev_step_ms, 4),
         "mask_plus_perm_over_attn": round(aux_ms / stage_ms["sparse_attn"], 4),
-        "hbm_gbs": ({
+        "hbm_gbs": (dict({
             "permute_fp8_qk": round(2 * perm8_bytes / (stage_ms["permute_fp8_qk"] / 1e3) / 1e9, 1),
             "permute_fp8_v": round(perm8v_bytes / (stage_ms["permute_fp8_v"] / 1e3) / 1e9, 1),
-            "unpermute": round(unperm_bytes / (stage_ms["unpermute"] / 1e3) / 1e9, 1),
-        } if a.fp8 else {
+        }, **({} if fused else {
+            "unpermute": round(unperm_bytes / (stage_ms["unpermute"] / 1e3) / 1e9, 1)}))
+            if a.fp8 else {
             "means_q_permute_means_k": round((means_bytes + perm_bytes) / (
                 stage_ms["means_q_permute_means_k"] / 1e3) / 1e9, 1),
             "permute_v": round(perm_bytes / (stage_ms["permute_v"] / 1e3) / 1e9, 1),
@@ -765,9 +774,9 @@ def measure(a, cfg, s, q, k, v):
         rf.permute(plan, q, out=qp)
         rf.permute(plan, k, out=kp)
         rf.permute(plan, v, order=rf.TILES_T, out=vt)
-        ref = rf.sparse_attn(plan, qp, kp, vt, kept, s)
+        ref = rf.unpermute(plan, rf.sparse_attn(plan, qp, kp, vt, kept, s))
         torch.cuda.synchronize()
-        diff = (op.float() - ref.float()).abs()
+        diff = (o.float() - ref.float()).abs()
         rec["fp8_vs_bf16_attention"] = {"max_abs": round(float(diff.max()), 5),
                                         "mean_abs": round(float(diff.mean()), 6)}
         rec["config"]["operands"] = ("e4m3: Q, K per-tile and V per-feature "

@@ -79,6 +79,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
     const uint8_t* __restrict__ k8, const float* __restrict__ k_scale,
     const uint8_t* __restrict__ v8, const float* __restrict__ v_scale,
     const int32_t* __restrict__ kept, __bf16* __restrict__ op, float* __restrict__ lse,
+    const int32_t* __restrict__ out_row, int64_t out_rows,
     const uint32_t* __restrict__ tile_bits, const int32_t* __restrict__ tile_count,
     int64_t Lt, int32_t BH, int32_t nb, int32_t n_tt, int32_t row_len_video, int64_t nnz,
     float scale_log2) {
@@ -397,9 +398,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
   const bool qvalid = (tile_bits[qtile * 4 + qs / 32] >> (qs % 32)) & 1u;
   const float inv = (qvalid && l_tot > 0.f) ? 1.f / l_tot : 0.f;
   const float ca = fa * inv, cb = fb * inv;
-  if (lse != nullptr && g == 0) lse[bh * Lt + qrow] = lse_of(m_t - kShift, l_tot, qvalid);
+  // Output row of this query slot: the slot itself, or (raster output) its
+  // raster token, -1 for a pad slot, which then has no output row.
+  const int64_t orow = out_row != nullptr ? int64_t(out_row[qrow]) : qrow;
+  if (orow < 0) return;
+  if (lse != nullptr && g == 0) lse[bh * out_rows + orow] = lse_of(m_t - kShift, l_tot, qvalid);
   // Lane (li, g) holds O^T[dd = db*32 + 8a + 4g + b][query li].
-  __bf16* dst = op + (bh * Lt + qrow) * D + 4 * g;
+  __bf16* dst = op + (bh * out_rows + orow) * D + 4 * g;
   const float* vsc = v_scale + bh * D + 4 * g;
   typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
   typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
@@ -422,7 +427,7 @@ rf_status attn_fp8(const rf_plan* plan, const void* q8, const float* q_scale, co
                    const float* k_scale, const void* v8, const float* v_scale,
                    const int32_t* kept, int32_t row_len_video, int64_t nnz, void* op,
                    float* lse, int32_t B, int32_t H, int32_t d, float scale, hipStream_t stream,
-                   const char* fn) {
+                   const char* fn, bool raster = false) {
   rf_status st = rf::check_call(plan, B, H, d, RF_BF16, fn);
   if (st != RF_OK) return st;
   if (d != D || plan->sz.bs != BS)
@@ -443,7 +448,8 @@ rf_status attn_fp8(const rf_plan* plan, const void* q8, const float* q_scale, co
   hipLaunchKernelGGL(attn_fp8_pp_kernel, dim3(BH * (nb + n_tt)), dim3(kThreads), 0, stream,
                      static_cast<const uint8_t*>(q8), q_scale, static_cast<const uint8_t*>(k8),
                      k_scale, static_cast<const uint8_t*>(v8), v_scale, kept,
-                     static_cast<__bf16*>(op), lse, plan->tile_bits, plan->tile_count,
+                     static_cast<__bf16*>(op), lse, raster ? plan->slot_src : nullptr,
+                     raster ? plan->sz.L : plan->sz.Lt, plan->tile_bits, plan->tile_count,
                      plan->sz.Lt, BH, nb, n_tt, row_len_video, nnz,
                      scale * 1.4426950408889634f);
   return rf::check_launch(fn);
@@ -465,6 +471,23 @@ extern "C" rf_status rf_sparse_attn_fp8(const rf_plan* plan, const void* q8,
   return attn_fp8(plan, q8, q_scale, k8, k_scale, v8, v_scale, kept_idx, kc.row_len_video,
                   kc.nnz_per_head, op, lse_or_null, B, H, d, scale, stream,
                   "rf_sparse_attn_fp8");
+}
+
+extern "C" rf_status rf_sparse_attn_fp8_raster(const rf_plan* plan, const void* q8,
+                                               const float* q_scale, const void* k8,
+                                               const float* k_scale, const void* v8,
+                                               const float* v_scale, const int32_t* kept_idx,
+                                               int32_t sparsity_pct, void* o, float* lse_or_null,
+                                               int32_t B, int32_t H, int32_t d, float scale,
+                                               hipStream_t stream) {
+  if (plan == nullptr)
+    return rf::fail(RF_ERR_INVALID_ARG, "rf_sparse_attn_fp8_raster: null plan");
+  rf_keep kc;
+  rf_status st = rf_layout_keep(&plan->lay, sparsity_pct, &kc);
+  if (st != RF_OK) return st;
+  return attn_fp8(plan, q8, q_scale, k8, k_scale, v8, v_scale, kept_idx, kc.row_len_video,
+                  kc.nnz_per_head, o, lse_or_null, B, H, d, scale, stream,
+                  "rf_sparse_attn_fp8_raster", true);
 }
 
 extern "C" rf_status rf_sparse_attn_fp8_rows(const rf_plan* plan, const void* q8,

@@ -102,6 +102,8 @@ _SIGNATURES = {
                            _vp, _c_i32, _c_i32, _c_i32, _c_f32, _vp],
     "rf_sparse_attn_fp8_rows": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i32,
                                 _vp, _vp, _c_i32, _c_i32, _c_i32, _c_f32, _vp],
+    "rf_sparse_attn_fp8_raster": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _vp,
+                                  _vp, _c_i32, _c_i32, _c_i32, _c_f32, _vp],
 }
 
 _lib = None
@@ -707,6 +709,29 @@ def sparse_attn_fp8(plan, q8, qs, k8, ks, v8, vs, kept, sparsity_pct, scale=None
     return (out, lo) if lse else out
 
 
+def sparse_attn_fp8_raster(plan, q8, qs, k8, ks, v8, vs, kept, sparsity_pct, scale=None,
+                           out=None, lse=False):
+    """rf_sparse_attn_fp8_raster: the FP8 attention with its bf16 output in
+    raster order [B, H, L, d] (and with lse=True the fp32 log-sum-exp
+    [B, H, L], raster order)."""
+    B, H, d = _fp8_operands(plan, q8, qs, k8, ks, v8, vs)
+    _kept_operand(plan, kept, B, H, sparsity_pct)
+    L = plan.sizes["L"]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, L, d), dtype=torch.bfloat16, device=q8.device)
+    _need(out, "out", (B, H, L, d), (torch.bfloat16,))
+    lo = torch.empty(B, H, L, dtype=torch.float32, device=q8.device) if lse else None
+    _check(lib().rf_sparse_attn_fp8_raster(plan.handle, _ptr(q8), _ptr(qs), _ptr(k8),
+                                           _ptr(ks), _ptr(v8), _ptr(vs), _ptr(kept),
+                                           int(sparsity_pct), _ptr(out),
+                                           _ptr(lo) if lse else None, B, H, d,
+                                           float(scale), _stream()),
+           "rf_sparse_attn_fp8_raster")
+    return (out, lo) if lse else out
+
+
 def sparse_attn_fp8_rows(plan, q8, qs, k8, ks, v8, vs, rows, scale=None, out=None,
                          lse=False):
     B, H, d = _fp8_operands(plan, q8, qs, k8, ks, v8, vs)
@@ -725,14 +750,19 @@ def sparse_attn_fp8_rows(plan, q8, qs, k8, ks, v8, vs, rows, scale=None, out=Non
     return (out, lo) if lse else out
 
 
-def sparse_attention_fp8(q, k, v, plan, sparsity_pct, scale=None):
+def sparse_attention_fp8(q, k, v, plan, sparsity_pct, scale=None, fused=True):
     """The whole path with the FP8 attention: permute into e4m3 codes and
-    pool (one pass per tensor), predict, attend, unpermute.  Returns
-    (o, kept)."""
+    pool (one pass per tensor), predict, attend.  fused=True writes the
+    output in raster order from the attention kernel; fused=False attends
+    in slot order and unpermutes (the same bytes).  Returns (o, kept)."""
     q8, qs, qbar = permute_fp8(plan, q, means=True)
     k8, ks, kbar = permute_fp8(plan, k, means=True)
     v8, vs = permute_fp8(plan, v, order=TILES_T)
     kept = predict_mask(plan, qbar, kbar, sparsity_pct)
+    if fused:
+        o = sparse_attn_fp8_raster(plan, q8, qs, k8, ks, v8, vs, kept, sparsity_pct,
+                                   scale=scale)
+        return o, kept
     op = sparse_attn_fp8(plan, q8, qs, k8, ks, v8, vs, kept, sparsity_pct, scale=scale)
     return unpermute(plan, op), kept
 

@@ -441,6 +441,21 @@ rf_status rf_sparse_attn_fp8(const rf_plan* plan, const void* q8,
                              int32_t B, int32_t H, int32_t d, float scale,
                              hipStream_t stream);
 
+/* rf_sparse_attn_fp8 writing its output in raster order, so that no
+ * rf_unpermute pass follows it: o bf16 [B][H][L][d] (L = N + n_text, text
+ * rows after the video rows) and lse_or_null fp32 [B][H][L], each row the
+ * value rf_sparse_attn_fp8 gives the slot holding that token, bit for bit;
+ * pad slots have no output row.  q8, k8, v8, the scales and kept_idx as
+ * for rf_sparse_attn_fp8 (the quantized Q stays in RF_ROWS slot order).
+ * Every row of o is written; the caller owns o. */
+rf_status rf_sparse_attn_fp8_raster(const rf_plan* plan, const void* q8,
+                                    const float* q_scale, const void* k8,
+                                    const float* k_scale, const void* v8,
+                                    const float* v_scale, const int32_t* kept_idx,
+                                    int32_t sparsity_pct, void* o, float* lse_or_null,
+                                    int32_t B, int32_t H, int32_t d, float scale,
+                                    hipStream_t stream);
+
 /* rf_sparse_attn_fp8 on padded kept rows (the layout of
  * rf_sparse_attn_rows). */
 rf_status rf_sparse_attn_fp8_rows(const rf_plan* plan, const void* q8,

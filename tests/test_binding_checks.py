@@ -152,6 +152,22 @@ def test_fp8_attention_refuses_mismatches(host):
         with pytest.raises(ValueError):
             rf.sparse_attn_fp8(p, a["q8"], a["qs"], a["k8"], a["ks"], a["v8"], a["vs"],
                                a["kept"], 20)
+    # The raster-output form: the same operand checks, and its output has
+    # one row per token, not per slot.
+    args = [good[k] for k in ("q8", "qs", "k8", "ks", "v8", "vs", "kept")]
+    with pytest.raises(AssertionError, match="rf_sparse_attn_fp8_raster reached"):
+        rf.sparse_attn_fp8_raster(p, *args, 20)
+    for name, over in bad.items():
+        a = dict(good, **over)
+        with pytest.raises(ValueError):
+            rf.sparse_attn_fp8_raster(p, a["q8"], a["qs"], a["k8"], a["ks"], a["v8"],
+                                      a["vs"], a["kept"], 20)
+    if z["Lt"] != z["L"]:
+        with pytest.raises(ValueError):
+            rf.sparse_attn_fp8_raster(p, *args, 20, out=torch.zeros(B, H, z["Lt"], d,
+                                                                    dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        rf.sparse_attn_fp8_raster(p, *args, 20, out=torch.zeros(B, H, z["L"], d))
 
 
 def test_other_entry_points_refuse_mismatches(host):

@@ -98,3 +98,51 @@ def test_fused_path_against_oracle():
     err = np.abs(parity.values(o) - want)
     assert err.max() <= parity.TOL["bf16"][0] and err.mean() <= parity.TOL["bf16"][1]
     plan.close()
+
+
+def _compare_fp8(lay, q, k, v, s):
+    plan = rf.Plan(lay)
+    o_f, kept_f = rf.sparse_attention_fp8(q, k, v, plan, s, fused=True)
+    o_u, kept_u = rf.sparse_attention_fp8(q, k, v, plan, s, fused=False)
+    q8, qs, _ = rf.permute_fp8(plan, q, means=True)
+    k8, ks, _ = rf.permute_fp8(plan, k, means=True)
+    v8, vs = rf.permute_fp8(plan, v, order=rf.TILES_T)
+    _, lse_slots = rf.sparse_attn_fp8(plan, q8, qs, k8, ks, v8, vs, kept_u, s, lse=True)
+    o_r, lse_raster = rf.sparse_attn_fp8_raster(plan, q8, qs, k8, ks, v8, vs, kept_u, s,
+                                                lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(kept_f, kept_u), "kept lists"
+    assert np.array_equal(parity.bits(o_f), parity.bits(o_u)), "fused FP8 output"
+    assert np.array_equal(parity.bits(o_r), parity.bits(o_u))
+    _, tok_slot, _, _ = rf.layout_tables(lay)
+    want = lse_slots[:, :, torch.from_numpy(tok_slot.astype(np.int64)).cuda()]
+    assert torch.equal(lse_raster.view(torch.int32), want.view(torch.int32)), "raster LSE"
+    plan.close()
+
+
+# The FP8 attention takes d = 128 and 128-slot tiles.
+FP8_CASES = [
+    ("ragged3d-text77", dict(T=3, H=13, W=21, wt=2, wh=8, ww=8, n_text=77, permute=1,
+                             sink=1), 2, 3, 70),
+    ("raster-bs128-text10", dict(T=3, H=7, W=11, wt=2, wh=8, ww=8, n_text=10, permute=0,
+                                 sink=1), 1, 2, 60),
+    ("frames-smaller-than-window", dict(T=4, H=3, W=5, wt=2, wh=8, ww=8, n_text=3,
+                                        permute=1, sink=1), 1, 2, 50),
+]
+
+
+@pytest.mark.parametrize("case", FP8_CASES, ids=[c[0] for c in FP8_CASES])
+def test_fused_fp8_path_equals_unpermuted_path(case):
+    name, lay, B, H, s = case
+    say(f"[fused fp8] {name} B={B} H={H} s={s}")
+    L = rf.layout_sizes(lay)["L"]
+    q, k, v = (inputs.random_tensor((B, H, L, 128), sd, device="cuda",
+                                    dtype=torch.bfloat16) for sd in (41, 42, 43))
+    _compare_fp8(lay, q, k, v, s)
+
+
+def test_fused_fp8_path_720p_four_heads():
+    cfg = configs.VIDEO720
+    say(f"[fused fp8] {cfg.name} 4 heads s=80")
+    q, k, v = inputs.make_qkv(cfg, "cuda", H=4)
+    _compare_fp8(cfg.layout, q, k, v, 80)
