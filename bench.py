@@ -437,11 +437,11 @@ def main():
     if a.raster:
         cfg = configs.SWEEP_RASTER if a.config in (3, 5) else cfg
     s = a.sparsity if a.sparsity is not None else (80 if a.config == 5 else cfg.sparsity[0])
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
     if a.heads is not None and not 1 <= a.heads <= cfg.H:
         print(f"--heads must be in 1..{cfg.H} for {cfg.name}", file=sys.stderr)
         return 2
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
     q, k, v = inputs.make_qkv(cfg, dev, H=a.heads)
     rec, exec_flop = measure(a, cfg, s, q, k, v)
     if not a.no_cpu_baseline:

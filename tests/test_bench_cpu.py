@@ -91,3 +91,12 @@ def test_clock_sampler_stays_off_under_a_profiler(monkeypatch):
     with bench.ClockSampler() as clock:
         time.sleep(0.01)
     assert clock.record() is None and calls == []
+
+
+def test_head_share_out_of_range_is_refused():
+    for h in ("0", "41"):
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--heads", h],
+                           capture_output=True, text=True, timeout=300, cwd=ROOT)
+        assert r.returncode == 2, r.stderr[-500:]
+        assert "--heads must be in 1..40" in r.stderr
+        assert r.stdout == ""
