@@ -482,6 +482,8 @@ extern "C" rf_status rf_sparse_attn_fp8_raster(const rf_plan* plan, const void* 
                                                hipStream_t stream) {
   if (plan == nullptr)
     return rf::fail(RF_ERR_INVALID_ARG, "rf_sparse_attn_fp8_raster: null plan");
+  if (o != nullptr && (o == q8 || o == k8 || o == v8))
+    return rf::fail(RF_ERR_INVALID_ARG, "rf_sparse_attn_fp8_raster: o must not overlap the operands");
   rf_keep kc;
   rf_status st = rf_layout_keep(&plan->lay, sparsity_pct, &kc);
   if (st != RF_OK) return st;

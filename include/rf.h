@@ -447,7 +447,8 @@ rf_status rf_sparse_attn_fp8(const rf_plan* plan, const void* q8,
  * value rf_sparse_attn_fp8 gives the slot holding that token, bit for bit;
  * pad slots have no output row.  q8, k8, v8, the scales and kept_idx as
  * for rf_sparse_attn_fp8 (the quantized Q stays in RF_ROWS slot order).
- * Every row of o is written; the caller owns o. */
+ * Every row of o is written; the caller owns o, which must not be one of
+ * the operand buffers (RF_ERR_INVALID_ARG). */
 rf_status rf_sparse_attn_fp8_raster(const rf_plan* plan, const void* q8,
                                     const float* q_scale, const void* k8,
                                     const float* k_scale, const void* v8,

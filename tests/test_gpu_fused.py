@@ -146,3 +146,33 @@ def test_fused_fp8_path_720p_four_heads():
     say(f"[fused fp8] {cfg.name} 4 heads s=80")
     q, k, v = inputs.make_qkv(cfg, "cuda", H=4)
     _compare_fp8(cfg.layout, q, k, v, 80)
+
+
+def test_raster_entries_refuse_an_output_over_an_operand():
+    """The raster-output entries read Q (or its codes) and write O in another
+    order, so O over an operand would be overwritten while it is read; the
+    library refuses it before any launch."""
+    import ctypes
+    lay = dict(T=2, H=9, W=17, wt=2, wh=8, ww=8, n_text=0, permute=1, sink=1)
+    plan = rf.Plan(lay)
+    z = plan.sizes
+    L = rf.lib()
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    q = torch.zeros(1, 1, z["L"], 128, dtype=torch.bfloat16, device="cuda")
+    kp = torch.zeros(1, 1, z["Lt"], 128, dtype=torch.bfloat16, device="cuda")
+    vt = torch.zeros(1, 1, z["n_tiles"], 128, z["bs"], dtype=torch.bfloat16, device="cuda")
+    kept = torch.zeros(1, 1, plan.keep(50)["nnz_per_head"], dtype=torch.int32, device="cuda")
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert L.rf_sparse_attn_raster(plan.handle, P(q), P(kp), P(vt), P(kept), 50, P(q), None,
+                                   1, 1, 128, 0.125, rf.BF16, st) == rf.ERR_INVALID_ARG
+    q8 = torch.zeros(1, 1, z["Lt"], 128, dtype=torch.uint8, device="cuda")
+    qs = torch.ones(1, 1, z["n_tiles"], device="cuda")
+    v8 = torch.zeros(1, 1, z["n_tiles"], 128, z["bs"], dtype=torch.uint8, device="cuda")
+    vs = torch.ones(1, 1, 128, device="cuda")
+    for over in (q8, v8):
+        assert L.rf_sparse_attn_fp8_raster(plan.handle, P(q8), P(qs), P(q8), P(qs), P(v8),
+                                           P(vs), P(kept), 50, P(over), None, 1, 1, 128,
+                                           0.125, st) == rf.ERR_INVALID_ARG
+    assert b"overlap" in L.rf_last_error()
+    torch.cuda.synchronize()
+    plan.close()
