@@ -490,7 +490,7 @@ class ClockSampler:
                 return
             found = self.PATTERN.findall(r.stdout)
             if found and not self._stop.is_set():
-                # The busiest GPU the tool lists (a box shows only its own).
+                # The busiest GPU the tool lists (on a one-GPU machine, that GPU).
                 self.samples.append(max(int(x) for x in found))
 
     def __exit__(self, *exc):
