@@ -450,11 +450,15 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
   f32x16 s[BS / 32];
   bf16x8 pb[BS / 32][2];
 
-  const uint32_t koff = dma_offset<C::kKRowBytes, C::kKRowBytes, C::kGroupWaves>(qw, lane);
-  const uint32_t voff = dma_offset<C::kVRowBytes, C::kVRowBytes, C::kGroupWaves>(qw, lane);
+  // Each wave copies a contiguous quarter of every K and V^T tile.
+  using KCopy = ContigTileCopy<C::kKRowBytes, C::kCopies>;
+  using VCopy = ContigTileCopy<C::kVRowBytes, C::kCopies>;
+  uint32_t klo[KCopy::P], vlo[VCopy::P];
+  KCopy::lane_offsets(lane, klo);
+  VCopy::lane_offsets(lane, vlo);
   auto copy_k = [&](int32_t kt) {
-    dma_tile<C::kCopies, C::kGroupWaves>(kh + int64_t(max(kt, 0)) * C::kTileBytes,
-                                         C::kTileBytes, ks, koff, qw);
+    const KCopy ck(kh + int64_t(max(kt, 0)) * C::kTileBytes, C::kTileBytes, ks, klo, qw);
+    static_for<C::kCopies>([&](auto u) { ck.template issue<decltype(u)::value>(); });
   };
 
   // LDS element offsets of this lane's operand chunks.
@@ -547,28 +551,36 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
   auto valu_phase = [&](int32_t i) {
     if (i < 0 || i >= n_own) return;
     const int32_t kt = kt_cur;
-    const bool next_k = i + 1 < n_own;
-    const TileCopy<C::kGroupWaves> ck(kh + int64_t(max(next_k ? kt_nxt : 0, 0)) *
-                                          C::kTileBytes, C::kTileBytes, ks, koff, qw);
-    const TileCopy<C::kGroupWaves> cv(vh + int64_t(max(kt, 0)) * C::kTileBytes, C::kTileBytes,
-                                      vsg, voff, qw);
-    static_assert(C::kCopies <= 8, "copy schedule below");
-    // Copies u of K(i+1) and V^T(i), each pair followed by a barrier to the
-    // scheduler so that the pairs stay spread through the softmax (a wave
-    // stalls at a copy while the memory pipeline is full, so a burst would
-    // hold back the arithmetic behind it).
-    auto copies = [&](auto u) {
-      constexpr int U = decltype(u)::value;
+    // K(i+1) is copied on the last step too (tile 0 then, never read): a
+    // branch around each copy costs more issue cycles than the copy.
+    const KCopy ck(kh + int64_t(i + 1 < n_own ? max(kt_nxt, 0) : 0) * C::kTileBytes,
+                   C::kTileBytes, ks, klo, qw);
+    const VCopy cv(vh + int64_t(max(kt, 0)) * C::kTileBytes, C::kTileBytes, vsg, vlo, qw);
+    static_assert(C::kCopies == 4 || C::kCopies == 8, "copy schedule below");
+    // Copy slot S of 8, each followed by a barrier to the scheduler so that
+    // the slots stay spread through the softmax (a wave stalls at a copy
+    // while the memory pipeline is full, so a burst would hold back the
+    // arithmetic behind it).  Slots take two copies each in the order K 0-3,
+    // V^T 0-3, K 4-7, V^T 4-7, so that the LDS base changes once per four
+    // copies.
+    auto copies = [&](auto slot) {
+      constexpr int S = decltype(slot)::value;
+      constexpr int U = (S / 4) * 4 + (S % 2) * 2;
       if constexpr (U < C::kCopies) {
-        if (next_k) ck.template issue<U>();
-        cv.template issue<U>();
+        if constexpr (S % 4 < 2) {
+          ck.template issue<U>();
+          ck.template issue<U + 1>();
+        } else {
+          cv.template issue<U>();
+          cv.template issue<U + 1>();
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    if (next_k) poison_tile<C::kCopies, C::kGroupWaves>(ks, qw, lane);
-    poison_tile<C::kCopies, C::kGroupWaves>(vsg, qw, lane);
+    poison_share<C::kCopies>(ks, qw, lane);
+    poison_share<C::kCopies>(vsg, qw, lane);
     copies(I0{});
     // The next step's scalars (in flight during the softmax).
     const int32_t kt_n2 = tile_of(i + 2);
@@ -685,7 +697,7 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
   };
 
   if (n_own > 0) {
-    poison_tile<C::kCopies, C::kGroupWaves>(ks, qw, lane);
+    poison_share<C::kCopies>(ks, qw, lane);
     copy_k(kt_cur);
   }
   // Every scalar the loop reads is resident before it starts: a scalar load

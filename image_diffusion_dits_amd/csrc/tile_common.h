@@ -3,6 +3,8 @@
 // global -> LDS tile copies through buffer resources.
 #pragma once
 
+#include <type_traits>
+
 #include "rf_internal.h"
 
 namespace rf_tile {
@@ -65,6 +67,15 @@ __device__ inline uint32_t dma_offset(int w, int lane) {
   return uint32_t(r * GROW + (pc ^ swz_rows<RB>(r)) * 16);
 }
 
+// Calls f(std::integral_constant<int, u>) for u = U .. N-1, in order.
+template <int N, int U = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (U < N) {
+    f(std::integral_constant<int, U>{});
+    static_for<N, U + 1>(f);
+  }
+}
+
 // Word 3 of a raw buffer resource (untyped dword access) on gfx9-family
 // GPUs.
 constexpr int kBufferWord3 = 0x00020000;
@@ -91,28 +102,52 @@ __device__ __forceinline__ void dma_tile(const char* base, int bytes, void* dst,
         u * kStride, 0, 0);
 }
 
-// The copies of dma_tile issued one at a time, so that a caller can spread
-// them between other instructions: a wave stalls at a tile copy while the
-// memory pipeline is still taking the previous ones, so a burst of copies
-// holds back the arithmetic queued behind it.
-template <int WAVES>
-struct TileCopy {
+// Tile copies issued one at a time, so that a caller can spread them
+// between other instructions, with each group wave taking a contiguous
+// share of the tile: copy u of wave w writes LDS [dst + (w*COPIES + u)*1024,
+// +1024), the same LDS layout as dma_tile (row r at r * RB, its 16-byte
+// chunks swizzled by swz_rows), from the matching global bytes.  The
+// swizzle repeats every 16 rows, i.e. every P = RB / 64 copies, so the lane
+// offsets are P registers (lane_offsets).  A copy's instruction offset moves
+// its LDS and global addresses alike, by up to 3 KB, so four consecutive
+// copies share one LDS base (one write of M0 instead of four): copy u takes
+// base (u & ~3) KB into the wave's share and offset (u & 3) KB.
+template <int RB, int COPIES>
+struct ContigTileCopy {
+  static constexpr int P = RB / 64;
+  static_assert(P >= 1 && P <= 4 && COPIES % 4 == 0 && COPIES % P == 0,
+                "a wave's share starts on a swizzle period");
   __amdgpu_buffer_rsrc_t rsrc;
-  char* dst;
-  uint32_t voff;
-  __device__ __forceinline__ TileCopy(const char* base, int bytes, void* lds, uint32_t v, int w)
-      : rsrc(__builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, bytes, kBufferWord3)),
-        voff(v) {
-    int woff = w * 1024;
+  char* dst;           // LDS start of the wave's share
+  int soff;            // byte offset of the wave's share in the tile
+  uint32_t voff[P];
+  __device__ __forceinline__ ContigTileCopy(const char* base, int bytes, void* lds,
+                                            const uint32_t (&v)[P], int w)
+      : rsrc(__builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, bytes, kBufferWord3)) {
+#pragma unroll
+    for (int j = 0; j < P; ++j) voff[j] = v[j];
+    int woff = w * COPIES * 1024;
     asm volatile("" : "+s"(woff));
     dst = static_cast<char*>(lds) + woff;
+    soff = woff;
   }
-  // Copy u: LDS [dst + u*WAVES*1024, +1024) from lane offset voff + u * the
-  // bytes one copy covers, as in dma_tile.
+  // Lane offsets within a 1 KB copy for the P swizzle phases: lane l moves
+  // chunk l % (RB/16) of row l / (RB/16) of the piece, whose first row is
+  // 1024/RB * j modulo the 16-row period.
+  __device__ static void lane_offsets(int lane, uint32_t (&v)[P]) {
+    constexpr int cpr = RB / 16;
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      const int r = j * (1024 / RB) + lane / cpr;
+      v[j] = uint32_t((lane / cpr) * RB + ((lane % cpr) ^ swz_rows<RB>(r)) * 16);
+    }
+  }
   template <int U>
   __device__ __forceinline__ void issue() const {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + U * WAVES * 1024), 16,
-                                             voff, U * WAVES * 64 * 16, 0, 0);
+    static_assert(U >= 0 && U < COPIES, "copy index");
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + (U & ~3) * 1024), 16,
+                                             voff[U % P], soff + (U & ~3) * 1024,
+                                             (U & 3) * 1024, 0);
   }
 };
 
@@ -148,6 +183,22 @@ __device__ __forceinline__ void poison_tile(void* dst, int w, int lane) {
 #pragma unroll
   for (int u = 0; u < COPIES; ++u)
     *reinterpret_cast<uint4*>(d + u * WAVES * 1024) = nan;
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the fill is in LDS
+#else
+  (void)dst; (void)w; (void)lane;
+#endif
+}
+
+// poison_tile for the copies of ContigTileCopy: wave w's copy u writes
+// [dst + (w*COPIES + u) * 1024, +1024).
+template <int COPIES>
+__device__ __forceinline__ void poison_share(void* dst, int w, int lane) {
+#ifdef RF_POISON_LDS
+  const uint4 nan = make_uint4(0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu);
+  char* d = static_cast<char*>(dst) + w * COPIES * 1024 + lane * 16;
+#pragma unroll
+  for (int u = 0; u < COPIES; ++u)
+    *reinterpret_cast<uint4*>(d + u * 1024) = nan;
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the fill is in LDS
 #else
   (void)dst; (void)w; (void)lane;
