@@ -425,12 +425,13 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
   // part in every barrier but does no work in its missing step.
   const int32_t n_grp = (row_len + 1) / 2;
   const int32_t n_own = (row_len + 1 - grp) / 2;
-  // Kept tile of this group's tile i, or -1: entries past the end and ids out
-  // of range are walked as fully masked tiles (whose copies read tile 0).
+  // Kept tile of this group's step i, or -1 for an id out of range, which is
+  // walked as a fully masked tile (whose copies read tile 0).  Past the end
+  // of the row the last entry is read; such steps are never walked, and
+  // their tiles are read only where a step's existence is tested anyway.
   auto tile_of = [&](int32_t i) -> int32_t {
-    const int32_t j = 2 * i + grp;
-    const int32_t kt = row[max(min(j, row_len - 1), 0)];
-    return (j < row_len && kt >= 0 && kt < n_tiles) ? kt : -1;
+    const int32_t kt = row[max(min(2 * i + grp, row_len - 1), 0)];
+    return uint32_t(kt) < uint32_t(n_tiles) ? kt : -1;
   };
 
   // Q operand (B of S^T = K Q^T): lane (li, g) holds q[li][16m + 8g .. +8].
@@ -456,8 +457,14 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
   uint32_t klo[KCopy::P], vlo[VCopy::P];
   KCopy::lane_offsets(lane, klo);
   VCopy::lane_offsets(lane, vlo);
+  // One buffer resource per head for each of K and V^T; a tile's offset
+  // goes to the copies' scalar offset.
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(kh), 0, n_tiles * C::kTileBytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(vh), 0, n_tiles * C::kTileBytes, kBufferWord3);
   auto copy_k = [&](int32_t kt) {
-    const KCopy ck(kh + int64_t(max(kt, 0)) * C::kTileBytes, C::kTileBytes, ks, klo, qw);
+    const KCopy ck(krsrc, max(kt, 0) * C::kTileBytes, ks, klo, qw);
     static_for<C::kCopies>([&](auto u) { ck.template issue<decltype(u)::value>(); });
   };
 
@@ -483,8 +490,9 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
     __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
   };
 
-  // MFMA phase of tile i.
-  auto mfma_phase = [&](int32_t i) {
+  // MFMA phase of tile i: PV of tile i - 1 if pv, scores of tile i if sc
+  // (flags known at compile time where the walk's steady state allows).
+  auto mfma_phase = [&](auto pv, auto sc) {
     // The lane parts of the operand addresses pass through an empty asm at
     // each phase, so the swizzled addresses are derived here (a few VALU
     // instructions beside the MFMAs) instead of all being held in registers
@@ -495,7 +503,7 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
     asm volatile("" : "+v"(vlane), "+v"(vx), "+v"(klane), "+v"(kx));
     const char* const vs = reinterpret_cast<const char*>(vsg) + vlane;
     const char* const kq = reinterpret_cast<const char*>(ks) + klane;
-    if (i >= 1 && i - 1 < n_own) {
+    if (pv) {
       // O^T[db] += V^T[db rows, keys] P^T(i-1); MFMA (kb, h) takes keys
       // kb*32 + 16h + 8g .. +8 in lane group g.
 #pragma unroll
@@ -514,7 +522,7 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
     }
     // P(i-1) dies with the PV above before the scores of tile i are born.
     __builtin_amdgcn_sched_barrier(0);
-    if (i < n_own) {
+    if (sc) {
       // S^T blocks: s[kb] covers keys kb*32 .. +32 x the wave's 32 queries.
       // MFMA row x of block kb is fed K row kb*32 + sigma(x), so
       // accumulator register r = 4a + b of lane group g holds key
@@ -549,13 +557,11 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
   // VALU phase of tile i: the copies of K(i+1) and V^T(i) (their buffers
   // were last read in the MFMA phase just finished) and softmax(i).
   auto valu_phase = [&](int32_t i) {
-    if (i < 0 || i >= n_own) return;
     const int32_t kt = kt_cur;
     // K(i+1) is copied on the last step too (tile 0 then, never read): a
     // branch around each copy costs more issue cycles than the copy.
-    const KCopy ck(kh + int64_t(i + 1 < n_own ? max(kt_nxt, 0) : 0) * C::kTileBytes,
-                   C::kTileBytes, ks, klo, qw);
-    const VCopy cv(vh + int64_t(max(kt, 0)) * C::kTileBytes, C::kTileBytes, vsg, vlo, qw);
+    const KCopy ck(krsrc, (i + 1 < n_own ? max(kt_nxt, 0) : 0) * C::kTileBytes, ks, klo, qw);
+    const VCopy cv(vrsrc, max(kt, 0) * C::kTileBytes, vsg, vlo, qw);
     static_assert(C::kCopies == 4 || C::kCopies == 8, "copy schedule below");
     // Copy slot S of 8, each followed by a barrier to the scheduler so that
     // the slots stay spread through the softmax (a wave stalls at a copy
@@ -707,21 +713,25 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
                "s"(bits_cur.w), "s"(scale_log2), "s"(n_grp), "s"(n_own), "s"(row_len));
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __builtin_amdgcn_s_barrier();
-  // Phase pairs: group 0 runs MFMA(i) then VALU(i); group 1 runs VALU(i-1)
-  // then MFMA(i).  Both take the same number of barriers.  One loop per
-  // group, so that each loop carries either P or the scores, not both.
+  // Phase pairs i = 0 .. n_grp: group 0 runs MFMA(i) then VALU(i); group 1
+  // runs VALU(i-1) then MFMA(i).  MFMA(i) takes the PV of step i - 1 and the
+  // scores of step i where those steps are the group's own (i - 1 < n_own,
+  // i < n_own), and VALU(i) runs for i < n_own (n_own is n_grp for group 0).
+  // Both groups take the same number of barriers.  One loop per group, so
+  // that each loop carries either P or the scores, not both.
   if (grp == 0) {
     for (int32_t i = 0; i <= n_grp; ++i) {
-      mfma_phase(i);
+      mfma_phase(i >= 1, i < n_grp);
       __builtin_amdgcn_s_barrier();
-      valu_phase(i);
+      if (i < n_grp) valu_phase(i);
       __builtin_amdgcn_s_barrier();
     }
   } else {
     for (int32_t i = 0; i <= n_grp; ++i) {
-      valu_phase(i - 1);
+      const bool own_prev = i >= 1 && i - 1 < n_own;
+      if (own_prev) valu_phase(i - 1);
       __builtin_amdgcn_s_barrier();
-      mfma_phase(i);
+      mfma_phase(own_prev, i < n_own);
       __builtin_amdgcn_s_barrier();
     }
   }

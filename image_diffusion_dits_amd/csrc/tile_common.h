@@ -123,13 +123,21 @@ struct ContigTileCopy {
   uint32_t voff[P];
   __device__ __forceinline__ ContigTileCopy(const char* base, int bytes, void* lds,
                                             const uint32_t (&v)[P], int w)
-      : rsrc(__builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, bytes, kBufferWord3)) {
+      : ContigTileCopy(__builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, bytes,
+                                                         kBufferWord3),
+                       0, lds, v, w) {}
+  // The tile at byte offset tile_off of the buffer r covers (e.g. one head's
+  // tiles): the offset goes to the scalar offset, so the resource can stay
+  // the same for every tile.
+  __device__ __forceinline__ ContigTileCopy(__amdgpu_buffer_rsrc_t r, int tile_off, void* lds,
+                                            const uint32_t (&v)[P], int w)
+      : rsrc(r) {
 #pragma unroll
     for (int j = 0; j < P; ++j) voff[j] = v[j];
     int woff = w * COPIES * 1024;
     asm volatile("" : "+s"(woff));
     dst = static_cast<char*>(lds) + woff;
-    soff = woff;
+    soff = tile_off + woff;
   }
   // Lane offsets within a 1 KB copy for the P swizzle phases: lane l moves
   // chunk l % (RB/16) of row l / (RB/16) of the piece, whose first row is
