@@ -112,10 +112,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
   // does no work in the missing one (it still takes part in the barriers).
   const int32_t n_grp = (row_len + 1) / 2;
   const int32_t n_own = (row_len + 1 - grp) / 2;
+  // Kept tile of this group's step i, or -1 for an id out of range (walked
+  // as a fully masked tile).  Past the end of the row the last entry is
+  // read; such steps are never walked, and their tiles are read only where
+  // a step's existence is tested anyway.
   auto tile_of = [&](int32_t i) -> int32_t {
-    const int32_t j = 2 * i + grp;
-    const int32_t kt = row[max(min(j, row_len - 1), 0)];
-    return (j < row_len && kt >= 0 && kt < n_tiles) ? kt : -1;
+    const int32_t kt = row[max(min(2 * i + grp, row_len - 1), 0)];
+    return uint32_t(kt) < uint32_t(n_tiles) ? kt : -1;
   };
 
   // Q operand (B of S^T = K Q^T): lane (li, g) holds q[li][64m + 32g .. +32].
@@ -146,13 +149,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
   const uint32_t koff = uint32_t(key0 * kRowBytes + (pc ^ swz_rows<kRowBytes>(xr)) * 16);
   const uint32_t ksoff[kCopies] = {0u, 16u * kRowBytes, 64u * kRowBytes, 80u * kRowBytes};
   const uint32_t voff = dma_offset<kRowBytes, kRowBytes, kGroupWaves>(qw, lane);
+  // One buffer resource per head for each of K and V^T; a tile's offset
+  // goes to the copies' scalar offset.
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(kh), 0, n_tiles * kTileBytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(vh), 0, n_tiles * kTileBytes, kBufferWord3);
   auto copy_k = [&](int32_t kt, int par) {
-    dma_tile_perm<kCopies, kGroupWaves>(kh + int64_t(max(kt, 0)) * kTileBytes, kTileBytes,
-                                        kslot + par * kTileBytes, koff, qw, ksoff);
+    dma_tile_perm_at<kCopies, kGroupWaves>(krsrc, max(kt, 0) * kTileBytes,
+                                           kslot + par * kTileBytes, koff, qw, ksoff);
   };
   auto copy_v = [&](int32_t kt, int par) {
-    dma_tile<kCopies, kGroupWaves>(vh + int64_t(max(kt, 0)) * kTileBytes, kTileBytes,
-                                   vslot + par * kTileBytes, voff, qw);
+    dma_tile_at<kCopies, kGroupWaves>(vrsrc, max(kt, 0) * kTileBytes, vslot + par * kTileBytes,
+                                      voff, qw);
   };
   const int rswz = swz_rows<kRowBytes>(li);     // rows 32 kb + li and 32 db + li
   // 32 bytes of row r at 16-byte chunks c0 and c0 + 1 (c0 = 4 step + 2g): the
@@ -218,11 +227,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
   // runs: in the phase where group 1 issues MFMAs beside group 0's softmax,
   // its MFMAs waited for issue slots and that phase took about 700 cycles
   // more than the other (per step, 720p video).
-  auto mfma_phase = [&](int32_t i) {
+  // MFMA phase of step i: PV of step i - 1 if pv, scores of step i if sc.
+  auto mfma_phase = [&](int32_t i, bool pv, bool sc) {
     __builtin_amdgcn_s_setprio(3);
     int lrow = li * kRowBytes, x0 = ((2 * g) ^ rswz) * 16, x1 = ((2 * g + 1) ^ rswz) * 16;
     asm volatile("" : "+v"(lrow), "+v"(x0), "+v"(x1));
-    if (i >= 1 && i - 1 < n_own) {
+    if (pv) {
       // O^T[db] += V^T[db rows, keys 64s .. +64] P^T(i-1), k-steps s = 0, 1.
       const uint8_t* const vs = vslot + ((i - 1) & 1) * kTileBytes + lrow;
 #pragma unroll
@@ -235,7 +245,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
       lsum = mma(row_sum_operand(1), pb[1], lsum);
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (i < n_own) {
+    if (sc) {
       const uint8_t* const ks = kslot + (i & 1) * kTileBytes + lrow;
 #pragma unroll
       for (int kb = 0; kb < BS / 32; ++kb) {
@@ -261,7 +271,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
   };
 
   auto valu_phase = [&](int32_t i) {
-    if (i < 0 || i >= n_own) return;
     const int32_t kt = kt_cur;
     // The next step's scalars (in flight during the softmax).
     const int32_t kt_n2 = tile_of(i + 2);
@@ -356,18 +365,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_pp_kernel(
                "s"(row_len));
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __builtin_amdgcn_s_barrier();
+  // Phase pairs i = 0 .. n_grp: MFMA(i) takes the PV of step i - 1 and the
+  // scores of step i where those steps are the group's own (i - 1 < n_own,
+  // i < n_own; n_own is n_grp for group 0), and VALU(i) runs for i < n_own.
   if (grp == 0) {
     for (int32_t i = 0; i <= n_grp; ++i) {
-      mfma_phase(i);
+      mfma_phase(i, i >= 1, i < n_grp);
       __builtin_amdgcn_s_barrier();
-      valu_phase(i);
+      if (i < n_grp) valu_phase(i);
       __builtin_amdgcn_s_barrier();
     }
   } else {
     for (int32_t i = 0; i <= n_grp; ++i) {
-      valu_phase(i - 1);
+      const bool own_prev = i >= 1 && i - 1 < n_own;
+      if (own_prev) valu_phase(i - 1);
       __builtin_amdgcn_s_barrier();
-      mfma_phase(i);
+      mfma_phase(i, own_prev, i < n_own);
       __builtin_amdgcn_s_barrier();
     }
   }

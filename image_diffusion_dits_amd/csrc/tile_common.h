@@ -80,18 +80,17 @@ __device__ __forceinline__ void static_for(F&& f) {
 // GPUs.
 constexpr int kBufferWord3 = 0x00020000;
 
-// Copies one tile of `bytes` bytes at `base` into LDS at `dst` through a
-// buffer resource spanning exactly the tile: copy u of group wave w writes
+// Copies one tile into LDS at `dst`: the tile at byte offset tile_off of the
+// buffer rsrc covers (dma_tile: the tile of `bytes` bytes at `base`, through a
+// resource spanning exactly the tile).  Copy u of group wave w writes
 // LDS [dst + (u*WAVES + w) * 1024, +1024) from lane offset voff + u * the
 // bytes one copy covers.  The wave's offset passes through an empty asm so
 // that the compiler recomputes the LDS addresses at each call instead of
 // keeping every one of them in a scalar register across the loop (which
 // spilled them to VGPR lanes).
 template <int COPIES, int WAVES>
-__device__ __forceinline__ void dma_tile(const char* base, int bytes, void* dst,
-                                         uint32_t voff, int w) {
-  const __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, bytes, kBufferWord3);
+__device__ __forceinline__ void dma_tile_at(__amdgpu_buffer_rsrc_t rsrc, int tile_off,
+                                            void* dst, uint32_t voff, int w) {
   constexpr int kStride = WAVES * 64 * 16;
   int woff = w * 1024;
   asm volatile("" : "+s"(woff));
@@ -99,7 +98,14 @@ __device__ __forceinline__ void dma_tile(const char* base, int bytes, void* dst,
   for (int u = 0; u < COPIES; ++u)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rsrc, (lds_void*)(static_cast<char*>(dst) + woff + u * WAVES * 1024), 16, voff,
-        u * kStride, 0, 0);
+        tile_off + u * kStride, 0, 0);
+}
+template <int COPIES, int WAVES>
+__device__ __forceinline__ void dma_tile(const char* base, int bytes, void* dst,
+                                         uint32_t voff, int w) {
+  dma_tile_at<COPIES, WAVES>(
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, bytes, kBufferWord3), 0,
+      dst, voff, w);
 }
 
 // Tile copies issued one at a time, so that a caller can spread them
@@ -159,21 +165,19 @@ struct ContigTileCopy {
   }
 };
 
-// As dma_tile, with copy u reading from lane offset voff + soff[u]: for
+// As dma_tile_at, with copy u reading from lane offset voff + soff[u]: for
 // tiles whose LDS rows are a permutation of the global rows.
 template <int COPIES, int WAVES>
-__device__ __forceinline__ void dma_tile_perm(const char* base, int bytes, void* dst,
-                                              uint32_t voff, int w,
-                                              const uint32_t (&soff)[COPIES]) {
-  const __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, bytes, kBufferWord3);
+__device__ __forceinline__ void dma_tile_perm_at(__amdgpu_buffer_rsrc_t rsrc, int tile_off,
+                                                 void* dst, uint32_t voff, int w,
+                                                 const uint32_t (&soff)[COPIES]) {
   int woff = w * 1024;
   asm volatile("" : "+s"(woff));
 #pragma unroll
   for (int u = 0; u < COPIES; ++u)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rsrc, (lds_void*)(static_cast<char*>(dst) + woff + u * WAVES * 1024), 16, voff,
-        soff[u], 0, 0);
+        tile_off + soff[u], 0, 0);
 }
 
 // Debug build (-DRF_POISON_LDS): before a wave's tile copy lands, the LDS
