@@ -492,7 +492,11 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
 
   // MFMA phase of tile i: PV of tile i - 1 if pv, scores of tile i if sc
   // (flags known at compile time where the walk's steady state allows).
+  // The wave in its MFMA phase takes issue priority over the softmax wave on
+  // its SIMD, so that the matrix core is fed first when both have an
+  // instruction ready.
   auto mfma_phase = [&](auto pv, auto sc) {
+    __builtin_amdgcn_s_setprio(3);
     // The lane parts of the operand addresses pass through an empty asm at
     // each phase, so the swizzled addresses are derived here (a few VALU
     // instructions beside the MFMAs) instead of all being held in registers
@@ -541,6 +545,7 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
       }
       pipeline_reads();
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Per-tile scalars of this group's walk, carried in SGPRs: the kept tiles
