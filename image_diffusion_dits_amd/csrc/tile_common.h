@@ -81,8 +81,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 constexpr int kBufferWord3 = 0x00020000;
 
 // Copies one tile into LDS at `dst`: the tile at byte offset tile_off of the
-// buffer rsrc covers (dma_tile: the tile of `bytes` bytes at `base`, through a
-// resource spanning exactly the tile).  Copy u of group wave w writes
+// buffer rsrc covers.  Copy u of group wave w writes
 // LDS [dst + (u*WAVES + w) * 1024, +1024) from lane offset voff + u * the
 // bytes one copy covers.  The wave's offset passes through an empty asm so
 // that the compiler recomputes the LDS addresses at each call instead of
@@ -100,18 +99,11 @@ __device__ __forceinline__ void dma_tile_at(__amdgpu_buffer_rsrc_t rsrc, int til
         rsrc, (lds_void*)(static_cast<char*>(dst) + woff + u * WAVES * 1024), 16, voff,
         tile_off + u * kStride, 0, 0);
 }
-template <int COPIES, int WAVES>
-__device__ __forceinline__ void dma_tile(const char* base, int bytes, void* dst,
-                                         uint32_t voff, int w) {
-  dma_tile_at<COPIES, WAVES>(
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, bytes, kBufferWord3), 0,
-      dst, voff, w);
-}
 
 // Tile copies issued one at a time, so that a caller can spread them
 // between other instructions, with each group wave taking a contiguous
 // share of the tile: copy u of wave w writes LDS [dst + (w*COPIES + u)*1024,
-// +1024), the same LDS layout as dma_tile (row r at r * RB, its 16-byte
+// +1024), the same LDS layout as dma_tile_at (row r at r * RB, its 16-byte
 // chunks swizzled by swz_rows), from the matching global bytes.  The
 // swizzle repeats every 16 rows, i.e. every P = RB / 64 copies, so the lane
 // offsets are P registers (lane_offsets).  A copy's instruction offset moves
@@ -127,14 +119,9 @@ struct ContigTileCopy {
   char* dst;           // LDS start of the wave's share
   int soff;            // byte offset of the wave's share in the tile
   uint32_t voff[P];
-  __device__ __forceinline__ ContigTileCopy(const char* base, int bytes, void* lds,
-                                            const uint32_t (&v)[P], int w)
-      : ContigTileCopy(__builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, bytes,
-                                                         kBufferWord3),
-                       0, lds, v, w) {}
   // The tile at byte offset tile_off of the buffer r covers (e.g. one head's
-  // tiles): the offset goes to the scalar offset, so the resource can stay
-  // the same for every tile.
+  // tiles): the offset goes to the scalar offset, so the resource stays the
+  // same for every tile.
   __device__ __forceinline__ ContigTileCopy(__amdgpu_buffer_rsrc_t r, int tile_off, void* lds,
                                             const uint32_t (&v)[P], int w)
       : rsrc(r) {
