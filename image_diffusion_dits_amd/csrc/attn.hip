@@ -490,12 +490,11 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(
     __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
   };
 
-  // MFMA phase of tile i: PV of tile i - 1 if pv, scores of tile i if sc
-  // (flags known at compile time where the walk's steady state allows).
+  // MFMA phase of step i: PV of step i - 1 if pv, scores of step i if sc.
   // The wave in its MFMA phase takes issue priority over the softmax wave on
   // its SIMD, so that the matrix core is fed first when both have an
   // instruction ready.
-  auto mfma_phase = [&](auto pv, auto sc) {
+  auto mfma_phase = [&](bool pv, bool sc) {
     __builtin_amdgcn_s_setprio(3);
     // The lane parts of the operand addresses pass through an empty asm at
     // each phase, so the swizzled addresses are derived here (a few VALU
