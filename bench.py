@@ -95,6 +95,11 @@ def parse():
                     help="time the workload on this many heads instead of all: one "
                          "GPU's share when the heads are split across GPUs (the "
                          "720p workload's 40 heads over 8 GPUs is --heads 5)")
+    ap.add_argument("--clock-vs-data", action="store_true",
+                    help="instead of the step benchmark, time the bf16 attention on "
+                         "the same kept tiles with the synthetic operands, with Q and K "
+                         "scaled by 0.01, and with all-zero operands, each with the "
+                         "shader clock it holds and the cycles per call that gives")
     ap.add_argument("--reference-gemm", action="store_true",
                     help="instead of the step benchmark, time the vendor library's "
                          "dense bf16 GEMM (torch.matmul, 8192^3) on the same GPU, "
@@ -316,6 +321,73 @@ def reference_gemm(n=8192, calls=50):
     return 0
 
 
+def clock_study(a):
+    """The bf16 attention of one workload on three sets of operands that
+    share the synthetic data's kept tiles: the synthetic operands, Q and K
+    scaled by 0.01 (near-uniform weights), and all-zero operands.  The work
+    (tiles, copies, instructions) is the same; the power drawn, and so the
+    clock the chip holds, is not.  Each point runs for about two seconds
+    with the clock sampled, and reports ms per call, the frac against the
+    2.4 GHz peak, and cycles per call (ms x the median clock)."""
+    import torch
+
+    from image_diffusion_dits_amd import configs, inputs, rf
+
+    cfg = configs.get(a.config)
+    s = a.sparsity if a.sparsity is not None else (80 if a.config == 5 else cfg.sparsity[0])
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    q, k, v = inputs.make_qkv(cfg, dev, H=a.heads)
+    if q.dtype != torch.bfloat16:
+        print(f"--clock-vs-data times the bf16 attention; {cfg.name} is {q.dtype}",
+              file=sys.stderr)
+        return 2
+    plan = rf.Plan(cfg.layout)
+    z = plan.sizes
+    B, H, d = q.shape[0], q.shape[1], q.shape[3]
+    qp, qbar = rf.permute_means(plan, q)
+    kp, kbar = rf.permute_means(plan, k)
+    vt = rf.permute(plan, v, order=rf.TILES_T)
+    kept = rf.predict_mask(plan, qbar, kbar, s)
+    flop = 4.0 * d * z["bs"] ** 2 * plan.keep(s)["nnz_per_head"] * B * H
+    sets = [("synthetic", qp, kp, vt),
+            ("q_k_times_0.01", qp * 0.01, kp * 0.01, vt),
+            ("zeros", torch.zeros_like(qp), torch.zeros_like(kp), torch.zeros_like(vt))]
+    points = []
+    for name, qq, kk, vv in sets:
+        out = torch.empty_like(qq)
+        for _ in range(3):
+            rf.sparse_attn(plan, qq, kk, vv, kept, s, out=out)
+        torch.cuda.synchronize()
+        clock = ClockSampler()
+        calls = 0
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with clock:
+            e0.record()
+            t_end = time.perf_counter() + 2.0
+            while time.perf_counter() < t_end:
+                for _ in range(5):
+                    rf.sparse_attn(plan, qq, kk, vv, kept, s, out=out)
+                calls += 5
+                torch.cuda.synchronize()
+            e1.record()
+            torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / calls
+        clk = clock.record()
+        points.append({"operands": name, "ms_per_call": round(ms, 4), "calls": calls,
+                       "frac": round(flop / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                       "sclk_mhz": clk,
+                       "cycles_per_call": (round(ms * clk["median"] * 1e3) if clk else None)})
+        print(f"[clock] {name}: {points[-1]}", file=sys.stderr, flush=True)
+        del out
+    plan.close()
+    print(json.dumps({"metric": "bf16 attention time and shader clock against operand values",
+                      "workload": cfg.name, "sparsity_pct": s, "heads": H,
+                      "exec_tflop_per_call": round(flop / 1e12, 4), "points": points}),
+          flush=True)
+    return 0
+
+
 def source_hash(kernel):
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kernel]:
@@ -422,6 +494,8 @@ def main():
         return pattern_study()
     if a.reference_gemm:
         return reference_gemm()
+    if a.clock_vs_data:
+        return clock_study(a)
     if a.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported "
               "(every step is independent per head; the multi-GPU layout is "
