@@ -96,10 +96,11 @@ def parse():
                          "GPU's share when the heads are split across GPUs (the "
                          "720p workload's 40 heads over 8 GPUs is --heads 5)")
     ap.add_argument("--clock-vs-data", action="store_true",
-                    help="instead of the step benchmark, time the bf16 attention on "
-                         "the same kept tiles with the synthetic operands, with Q and K "
-                         "scaled by 0.01, and with all-zero operands, each with the "
-                         "shader clock it holds and the cycles per call that gives")
+                    help="instead of the step benchmark, time the bf16 attention (with "
+                         "--fp8 the FP8 one) on the same kept tiles with the synthetic "
+                         "operands, with Q and K scaled by 0.01, and with all-zero "
+                         "operands, each with the shader clock it holds and the cycles "
+                         "per call that gives")
     ap.add_argument("--reference-gemm", action="store_true",
                     help="instead of the step benchmark, time the vendor library's "
                          "dense bf16 GEMM (torch.matmul, 8192^3) on the same GPU, "
@@ -328,7 +329,8 @@ def clock_study(a):
     (tiles, copies, instructions) is the same; the power drawn, and so the
     clock the chip holds, is not.  Each point runs for about two seconds
     with the clock sampled, and reports ms per call, the frac against the
-    2.4 GHz peak, and cycles per call (ms x the median clock)."""
+    2.4 GHz peak, and cycles per call (ms x the median clock).  With --fp8
+    the FP8 attention runs instead, on each set's e4m3 codes."""
     import torch
 
     from image_diffusion_dits_amd import configs, inputs, rf
@@ -339,9 +341,10 @@ def clock_study(a):
     torch.cuda.set_device(dev)
     q, k, v = inputs.make_qkv(cfg, dev, H=a.heads)
     if q.dtype != torch.bfloat16:
-        print(f"--clock-vs-data times the bf16 attention; {cfg.name} is {q.dtype}",
+        print(f"--clock-vs-data times the bf16 or FP8 attention; {cfg.name} is {q.dtype}",
               file=sys.stderr)
         return 2
+    peak = PEAK_FP8_TFLOPS if a.fp8 else PEAK_BF16_TFLOPS
     plan = rf.Plan(cfg.layout)
     z = plan.sizes
     B, H, d = q.shape[0], q.shape[1], q.shape[3]
@@ -356,8 +359,14 @@ def clock_study(a):
     points = []
     for name, qq, kk, vv in sets:
         out = torch.empty_like(qq)
+        if a.fp8:
+            ops = (*rf.quantize_fp8(plan, qq), *rf.quantize_fp8(plan, kk),
+                   *rf.quantize_fp8(plan, vv, order=rf.TILES_T))
+            call = lambda: rf.sparse_attn_fp8(plan, *ops, kept, s, out=out)
+        else:
+            call = lambda: rf.sparse_attn(plan, qq, kk, vv, kept, s, out=out)
         for _ in range(3):
-            rf.sparse_attn(plan, qq, kk, vv, kept, s, out=out)
+            call()
         torch.cuda.synchronize()
         clock = ClockSampler()
         calls = 0
@@ -367,7 +376,7 @@ def clock_study(a):
             t_end = time.perf_counter() + 2.0
             while time.perf_counter() < t_end:
                 for _ in range(5):
-                    rf.sparse_attn(plan, qq, kk, vv, kept, s, out=out)
+                    call()
                 calls += 5
                 torch.cuda.synchronize()
             e1.record()
@@ -375,13 +384,14 @@ def clock_study(a):
         ms = e0.elapsed_time(e1) / calls
         clk = clock.record()
         points.append({"operands": name, "ms_per_call": round(ms, 4), "calls": calls,
-                       "frac": round(flop / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                       "frac": round(flop / (ms / 1e3) / 1e12 / peak, 4),
                        "sclk_mhz": clk,
                        "cycles_per_call": (round(ms * clk["median"] * 1e3) if clk else None)})
         print(f"[clock] {name}: {points[-1]}", file=sys.stderr, flush=True)
         del out
     plan.close()
-    print(json.dumps({"metric": "bf16 attention time and shader clock against operand values",
+    kind = "FP8" if a.fp8 else "bf16"
+    print(json.dumps({"metric": f"{kind} attention time and shader clock against operand values",
                       "workload": cfg.name, "sparsity_pct": s, "heads": H,
                       "exec_tflop_per_call": round(flop / 1e12, 4), "points": points}),
           flush=True)
