@@ -336,14 +336,14 @@ def clock_study(a):
     from image_diffusion_dits_amd import configs, inputs, rf
 
     cfg = configs.get(a.config)
+    if cfg.dtype != "bf16":
+        print(f"--clock-vs-data times the bf16 or FP8 attention; {cfg.name} is {cfg.dtype}",
+              file=sys.stderr)
+        return 2
     s = a.sparsity if a.sparsity is not None else (80 if a.config == 5 else cfg.sparsity[0])
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     q, k, v = inputs.make_qkv(cfg, dev, H=a.heads)
-    if q.dtype != torch.bfloat16:
-        print(f"--clock-vs-data times the bf16 or FP8 attention; {cfg.name} is {q.dtype}",
-              file=sys.stderr)
-        return 2
     peak = PEAK_FP8_TFLOPS if a.fp8 else PEAK_BF16_TFLOPS
     plan = rf.Plan(cfg.layout)
     z = plan.sizes

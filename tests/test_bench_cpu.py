@@ -100,3 +100,14 @@ def test_head_share_out_of_range_is_refused():
         assert r.returncode == 2, r.stderr[-500:]
         assert "--heads must be in 1..40" in r.stderr
         assert r.stdout == ""
+
+
+def test_clock_study_refuses_an_fp32_workload():
+    """--clock-vs-data times the bf16 (or FP8) attention: the fp32 workload
+    is refused before any device is touched."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--clock-vs-data",
+                        "--config", "1"],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    assert "bf16 or FP8" in r.stderr
+    assert r.stdout == ""
