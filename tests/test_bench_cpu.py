@@ -1,5 +1,6 @@
 """Host logic of bench.py that runs without a GPU: the one-GPU guard, the
-shader-clock sampler and the source-keyed traffic record."""
+shader-clock sampler, the source-keyed traffic record and the argument
+guards of the head-share and clock studies."""
 import json
 import os
 import subprocess
